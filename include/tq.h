@@ -1,0 +1,147 @@
+/*
+ * tq.h -- C ABI of the TurboQuant KV-cache codec for AMD MI355X (gfx950).
+ *
+ * The codec is the one shown on the page "@mlx-bun/inference 0.0.0-stage ->
+ * 1.0.0", package/src/kernels/turboquant/ops.ts, with the constant tables of
+ * the page "mlx-bun 0.0.9 -> 0.0.11", src/mlx/turboquant-tables.ts:
+ *
+ *   values  (ops.ts encodeValues / decodeValues): multiply by the fixed +-1
+ *           sign vector, normalised fast Walsh-Hadamard transform along
+ *           head_dim, per-32-element RMS scale (stored fp16), divide by
+ *           (scale + 1e-8), Lloyd-Max bin index = number of boundaries below
+ *           the value, bit-packed. Decode: centroid * scale, inverse
+ *           transform, sign multiply.
+ *   keys    (ops.ts encodeKeys / decodeKeys): per-32-element min/max affine
+ *           quantisation in binary32 with fp16 scale and zero point, round
+ *           half to even, clip, bit-packed. Decode: (q + zero) * scale.
+ *   packing (ops.ts packBits / bit-packing section): element i of a row
+ *           occupies bits [i*bits, i*bits + bits) of the row's byte stream,
+ *           least significant bit first; 8-bit codes are plain bytes.
+ *
+ * Data layout. K and V are row-major [tokens, heads, head_dim]; batches fold
+ * into tokens. With R = tokens * heads and G = head_dim / 32 the codec
+ * reads and writes five planes, each row-major and contiguous:
+ *   k_codes [R, head_dim * k_bits / 8]  u8  (two's complement int8 codes when
+ *                                            k_signed, otherwise unsigned)
+ *   k_scale [R, G]  fp16 bits           k_zero [R, G]  fp16 bits
+ *   v_codes [R, head_dim * v_bits / 8]  u8
+ *   v_scale [R, G]  fp16 bits
+ * Because groups never cross a row, appending at token t is a call on
+ * pointers advanced by t * heads rows of each plane.
+ *
+ * Ownership and execution. Every pointer except `cfg`, `out`/`in`
+ * (host structs read during the call) is device memory owned by the caller.
+ * The library allocates nothing and keeps no per-call state. Calls enqueue
+ * kernels on `stream` (a hipStream_t; NULL is the default stream) and return
+ * without waiting. Argument errors are detected on the host before any
+ * launch and leave every buffer untouched; a failed launch returns
+ * TQ_E_HIP. Faults during execution surface at the caller's next
+ * synchronisation.
+ *
+ * Alignment: K/V inputs and decoded outputs 16-byte aligned, code planes
+ * 4-byte aligned, fp16 planes 2-byte aligned (TQ_E_ALIGN otherwise).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. The pages' operations throw on invalid arguments
+ * (ops.ts packedDim, fwht, encodeKeys, encodeValues, packBits); here each
+ * such case returns a code instead. */
+enum {
+    TQ_OK = 0,
+    TQ_E_NULL = 1,     /* a required pointer is NULL                          */
+    TQ_E_HEAD_DIM = 2, /* head_dim not in {64, 128, 256, 512}                 */
+    TQ_E_BITS = 3,     /* bits not in {2,3,4,5,8}, or k_signed with k_bits!=8 */
+    TQ_E_ALIGN = 4,    /* misaligned pointer, or dim * bits not a whole byte  */
+    TQ_E_DTYPE = 5,    /* dtype not TQ_F32 / TQ_BF16                          */
+    TQ_E_SHAPE = 6,    /* negative tokens, heads < 1, or row count overflow   */
+    TQ_E_HIP = 7       /* the HIP runtime reported an error at launch         */
+};
+
+/* Element types of K/V inputs and decoded outputs. */
+enum { TQ_F32 = 0, TQ_BF16 = 1 };
+
+/* Decode flags. */
+enum {
+    /* Return V still in the rotated domain, centroid * scale with no
+     * inverse transform (ops.ts decodeValuesRotated: attention is linear
+     * in V, so the caller may un-rotate the attention output instead). */
+    TQ_DECODE_ROTATED_V = 1
+};
+
+/* Codec configuration (ops.ts: head_dim, key bits and signedness, value
+ * bits). k_signed is only valid with k_bits == 8 (ops.ts encodeKeys doc). */
+typedef struct tq_config {
+    int32_t head_dim; /* 64, 128, 256 or 512                     */
+    int32_t k_bits;   /* 2, 3, 4, 5 or 8                          */
+    int32_t v_bits;   /* 2, 3, 4, 5 or 8 (Lloyd-Max table widths) */
+    int32_t k_signed; /* 0 or 1                                   */
+} tq_config;
+
+/* The five device planes (layout above). Members for a side that is not
+ * encoded or decoded may be NULL. */
+typedef struct tq_packed_kv {
+    void *k_codes;
+    void *k_scale;
+    void *k_zero;
+    void *v_codes;
+    void *v_scale;
+} tq_packed_kv;
+
+/* ops.ts packedDim: bytes per row for `dim` elements of `bits` each, i.e.
+ * dim * bits / 8. Returns -TQ_E_ALIGN when dim * bits is not a multiple of
+ * 8 and -TQ_E_BITS when bits is outside 1..8 or dim < 1. Host only. */
+int64_t tq_packed_dim(int32_t dim, int32_t bits);
+
+/* Static, NUL-terminated message for a status code (never NULL). */
+const char *tq_status_string(int32_t status);
+
+/* Encode K and V [tokens, heads, head_dim] of dtype `in_dtype` into the
+ * planes of `out` (ops.ts encodeKeys + packBits for K, encodeValues +
+ * packBits for V). Either `k` or `v` may be NULL to encode one side only;
+ * the planes of the other side are then not touched. tokens == 0 is a
+ * no-op. One launch covers both sides. */
+int32_t tq_encode_kv(const void *k, const void *v, int32_t in_dtype,
+                     int64_t tokens, int32_t heads, const tq_config *cfg,
+                     const tq_packed_kv *out, void *stream);
+
+/* Decode the planes of `in` back to K and V [tokens, heads, head_dim] of
+ * dtype `out_dtype` (ops.ts unpackBits + decodeKeys, unpackBits +
+ * decodeValues; TQ_BF16 is the pages' output dtype, TQ_F32 returns the
+ * binary32 value before that rounding). Either output may be NULL to skip
+ * that side. `flags` is 0 or TQ_DECODE_ROTATED_V. One launch decodes K and
+ * V of the same rows together (ops.ts tryDecodePackedKv). */
+int32_t tq_decode_kv(const tq_packed_kv *in, int64_t tokens, int32_t heads,
+                     const tq_config *cfg, void *k_out, void *v_out,
+                     int32_t out_dtype, int32_t flags, void *stream);
+
+/* ops.ts unrotateValues: apply the inverse rotation (normalised transform,
+ * then sign multiply) in binary32 to `rows` rows of `head_dim` elements
+ * and write them back in `dtype`. x and out may alias. */
+int32_t tq_unrotate_values(const void *x, void *out, int32_t dtype, int64_t rows,
+                           int32_t head_dim, void *stream);
+
+/* Host copies of the constant tables the kernels use, for callers that
+ * fuse decoding into their own kernels (turboquant-tables.ts LLOYD_MAX and
+ * SIGN_VECTORS). centroids receives 2^bits floats, boundaries 2^bits - 1;
+ * signs receives head_dim floats of +-1. Host only. */
+int32_t tq_lloyd_max_table(int32_t bits, float *centroids, float *boundaries);
+int32_t tq_sign_vector(int32_t head_dim, float *signs);
+
+/* Host evaluation of the value bin search exactly as the kernels run it
+ * (same code, compiled for the host): idx[i] = number of Lloyd-Max
+ * boundaries strictly below z[i] (ops.ts searchsorted). For checking the
+ * search on the CPU. Host only. */
+int32_t tq_value_bin_host(int32_t bits, const float *z, int64_t n, uint8_t *idx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

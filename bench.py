@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 METRIC = "KV tokens/sec encode+decode (d=128, 4-bit) and achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
 SRC = os.path.join(ROOT, "kv_cache_quantization_tq_amd", "csrc", "tq_codec.hip")
-TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC = os.path.join(ROOT, "profiles", "prefill_hbm_traffic.json")
 
 
 def log(*a):
@@ -70,6 +70,26 @@ def measured_traffic(kernel: str):
     return int(k["fetch_bytes"] + k["write_bytes"])
 
 
+def device_copy_gbps(torch, dev, mib=256, nbuf=6, reps=20):
+    """Read + write GB/s of torch's device-to-device copy over rotating
+    buffers (context for the roofline: what a plain streaming kernel
+    reaches on this GPU)."""
+    n = mib * 2 ** 20 // 4
+    bufs = [(torch.ones(n, device=dev), torch.empty(n, device=dev)) for _ in range(nbuf)]
+    for i in range(nbuf):
+        bufs[i][1].copy_(bufs[i][0])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        bufs[i % nbuf][1].copy_(bufs[i % nbuf][0])
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / reps
+    del bufs
+    return 2 * mib * 2 ** 20 / t / 1e9
+
+
 def cpu_baseline(w, k, v):
     import oracle as O
     from kv_cache_quantization_tq_amd import workloads as W
@@ -93,6 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for >= 1.5 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -138,6 +160,16 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -170,6 +202,12 @@ def main():
         f"{dec_gbps:.0f} GB/s ({dec_gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s)")
     log(f"step: {ms_per_step * 1e3:.1f} us")
 
+    # context: a plain device-to-device copy of the same size class on this GPU
+    copy_gbps = device_copy_gbps(torch, dev)
+    step_gbps = (enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9
+    log(f"whole step: {step_gbps:.0f} GB/s ({step_gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s); "
+        f"device copy reference {copy_gbps:.0f} GB/s")
+
     if enc_avg >= dec_avg:
         kern, nbytes, avg, gbps = "encode", enc_bytes, enc_avg, enc_gbps
     else:
@@ -201,7 +239,9 @@ def main():
                      "frac": gbps / PEAK_HBM_GBPS, "traffic": measured_traffic(kern),
                      "algorithmic_bytes": nbytes, "avg_kernel_us": avg * 1e3},
         "kernels": {"encode": {"avg_us": enc_avg * 1e3, "GBps": enc_gbps, "bytes": enc_bytes},
-                    "decode": {"avg_us": dec_avg * 1e3, "GBps": dec_gbps, "bytes": dec_bytes}},
+                    "decode": {"avg_us": dec_avg * 1e3, "GBps": dec_gbps, "bytes": dec_bytes},
+                    "step": {"GBps": step_gbps, "frac": step_gbps / PEAK_HBM_GBPS},
+                    "device_copy_reference_GBps": copy_gbps},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -29,6 +29,9 @@
  * Because groups never cross a row, appending at token t is a call on
  * pointers advanced by t * heads rows of each plane.
  *
+ * A call with zero rows (tokens == 0) validates the configuration and
+ * returns TQ_OK without touching any pointer.
+ *
  * Ownership and execution. Every pointer except `cfg`, `out`/`in`
  * (host structs read during the call) is device memory owned by the caller.
  * The library allocates nothing and keeps no per-call state. Calls enqueue
@@ -38,8 +41,9 @@
  * TQ_E_HIP. Faults during execution surface at the caller's next
  * synchronisation.
  *
- * Alignment: K/V inputs and decoded outputs 16-byte aligned, code planes
- * 4-byte aligned, fp16 planes 2-byte aligned (TQ_E_ALIGN otherwise).
+ * Alignment (TQ_E_ALIGN otherwise): K/V inputs and decoded outputs 16
+ * bytes; code planes 16 bytes for 4- and 8-bit codes, 8 bytes for 2-, 3-
+ * and 5-bit codes; fp16 planes 2 bytes.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -135,9 +139,10 @@ int32_t tq_lloyd_max_table(int32_t bits, float *centroids, float *boundaries);
 int32_t tq_sign_vector(int32_t head_dim, float *signs);
 
 /* Host evaluation of the value bin search exactly as the kernels run it
- * (same code, compiled for the host): idx[i] = number of Lloyd-Max
- * boundaries strictly below z[i] (ops.ts searchsorted). For checking the
- * search on the CPU. Host only. */
+ * (same code, compiled for the host: the table-driven search of the fast
+ * path for |z| <= 6, the clamped general search otherwise): idx[i] = number
+ * of Lloyd-Max boundaries strictly below z[i] (ops.ts searchsorted). For
+ * checking the search on the CPU. Host only. */
 int32_t tq_value_bin_host(int32_t bits, const float *z, int64_t n, uint8_t *idx);
 
 #ifdef __cplusplus

@@ -36,17 +36,31 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <mutex>
+#include <unordered_map>
 
 #include "tq.h"
 #include "tq_tables.h"
 
 namespace {
 
+// Compile-time tuning knobs (defaults are the measured best on MI355X):
+//   TQ_ENCODE_PREFETCH_K  load the next tile's keys while encoding values;
+//   TQ_ENCODE_WAVES       if > 0, target this many wavefronts per SIMD
+//                         (caps the registers the encoder may use).
+#ifndef TQ_ENCODE_PREFETCH_K
+#define TQ_ENCODE_PREFETCH_K 1
+#endif
+#ifndef TQ_ENCODE_WAVES
+#define TQ_ENCODE_WAVES 0
+#endif
+
 constexpr int kGroup = 32;
 constexpr int kWave = 64;
 constexpr int kBlockThreads = 256;
 constexpr int kWavesPerBlock = kBlockThreads / kWave;
-constexpr int64_t kMaxBlocks = 8192;
 
 // ---------------------------------------------------------------------------
 // Constant tables
@@ -61,12 +75,20 @@ template <> struct LM<8> { static constexpr const float *c = kCentroids8; static
 
 constexpr double pow2(int e) { double r = 1.0; for (; e > 0; --e) r *= 2.0; for (; e < 0; ++e) r *= 0.5; return r; }
 
-// Uniform grid over the boundaries of the B-bit table. The cell of z is
-// clamp(floor(fma(z, A, C)), 0, N-1) with A = 1/W a power of two and
-// C = -LO*A, so z*A is exact and the fma rounds once; the computed cell of
-// any z lies within 2^-14 cells of its true position. Each cell stores the
-// number of boundaries below its (widened) lower edge and the one boundary,
-// if any, inside the widened cell; +inf when none.
+// Uniform grid over [-6, 6] for the B-bit table. The cell of z is
+// round-to-nearest-even(z*A + C), A = 1/W a power of two: z*A is exact and
+// one fma rounds, so the computed cell of any z is within 2^-14 cells of
+// its true position. On the device the fma adds 2^23 as well, which leaves
+// the cell index in the low mantissa bits of the result (floats in
+// [2^23, 2^24) are spaced by 1), so the LDS address is one shift-add of the
+// result's bit pattern. Each cell stores the number of boundaries below its
+// (widened) lower edge and the one boundary, if any, inside the widened
+// cell (+inf when none); W is below the smallest gap between adjacent
+// boundaries, so a widened cell never holds two. The kernels need no clamp:
+// a normalised value z = y / (rms + 1e-8) of a 32-element group satisfies
+// |z| <= sqrt(32) < 5.66 (each |y_j| is at most the group's root-sum-square),
+// and the first and last cells extend to -inf and +inf for the host
+// evaluation, which clamps.
 struct BinCell {
     float bnd;
     uint32_t base;
@@ -76,9 +98,12 @@ template <int B> struct BinGrid {
     static constexpr int NB = (1 << B) - 1;
     static constexpr float W = (float)pow2(LM<B>::cell_exp);
     static constexpr float A = (float)pow2(-LM<B>::cell_exp);
-    static constexpr float LO = LM<B>::b[0] - 0.5f * W;
-    static constexpr float C = -LO * A;
-    static constexpr int N = (int)((double)(LM<B>::b[NB - 1] - LO) * (double)A) + 2;
+    static constexpr float LO = -6.0f;
+    static constexpr float C = 6.0f * A;                 // cell c is centred at LO + c*W
+    static constexpr float C_MAGIC = C + 8388608.0f;     // + 2^23
+    static constexpr int N = (int)(12.0 * (double)A) + 2;
+    static_assert(LM<B>::b[0] > -5.9f && LM<B>::b[NB - 1] < 5.9f, "boundaries inside the grid");
+    static_assert(C_MAGIC - 8388608.0f == C, "grid offset exact");
 };
 
 template <int B> struct BinLut {
@@ -89,8 +114,8 @@ template <int B> struct BinLut {
         using Gr = BinGrid<B>;
         constexpr double margin = 1.0 / 1024.0;
         for (int c = 0; c < Gr::N; ++c) {
-            const double lo = (c == 0) ? -1e300 : (double)Gr::LO + ((double)c - margin) * (double)Gr::W;
-            const double hi = (c == Gr::N - 1) ? 1e300 : (double)Gr::LO + ((double)c + 1.0 + margin) * (double)Gr::W;
+            const double lo = (c == 0) ? -1e300 : (double)Gr::LO + ((double)c - 0.5 - margin) * (double)Gr::W;
+            const double hi = (c == Gr::N - 1) ? 1e300 : (double)Gr::LO + ((double)c + 0.5 + margin) * (double)Gr::W;
             uint32_t base = 0;
             int inside = 0;
             float bnd = __builtin_huge_valf();
@@ -209,26 +234,6 @@ __device__ __forceinline__ uint32_t sign_pair_mask(uint32_t smask, int k)
 // Walsh-Hadamard transform of one row held as 32 registers per lane
 // ---------------------------------------------------------------------------
 
-// value of lane (lane ^ M) for M in {1,2,4,8}; all patterns stay inside a
-// 16-lane DPP row, hence inside one row team
-template <int M> __device__ __forceinline__ float lane_xor(float v);
-template <> __device__ __forceinline__ float lane_xor<1>(float v)
-{
-    return as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), 0xB1, 0xF, 0xF, true)); // quad_perm [1,0,3,2]
-}
-template <> __device__ __forceinline__ float lane_xor<2>(float v)
-{
-    return as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), 0x4E, 0xF, 0xF, true)); // quad_perm [2,3,0,1]
-}
-template <> __device__ __forceinline__ float lane_xor<4>(float v)
-{
-    return as_f((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_u(v), 0x101F)); // bitmask mode, xor 4
-}
-template <> __device__ __forceinline__ float lane_xor<8>(float v)
-{
-    return as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), 0x128, 0xF, 0xF, true)); // row_ror:8
-}
-
 // butterflies of span 1, 2, 4, 8, 16 inside the group
 __device__ __forceinline__ void fwht_in_lane(float (&y)[kGroup])
 {
@@ -247,60 +252,141 @@ __device__ __forceinline__ void fwht_in_lane(float (&y)[kGroup])
     }
 }
 
-// butterfly of span 32*M between group g and group g^M: the lower group
-// keeps a + b, the upper one b's partner minus itself, i.e. a - b
-template <int M> __device__ __forceinline__ void fwht_cross(float (&y)[kGroup], int g)
+// Butterflies of span 32*M between the groups g and g^M of a row team.
+//
+// Each lane keeps its values multiplied by a carried sign c = +-1 (the same
+// for all 32 registers of the lane), so that one fused multiply-add per
+// element does the butterfly: own + sigma * partner, where sigma = +1 in
+// the lower group and -1 in the upper one. The lower group then holds
+// c * (a + b) and the upper one -c * (a - b); since partners differ only in
+// bit M, which no earlier stage has touched, they carry equal signs, and the
+// fma (exact product by +-1, one rounding) rounds exactly as a + b or a - b.
+// After all stages c = (-1)^popcount(g), which the caller folds into the
+// final multiply by 1/sqrt(d).
+//
+// M = 1, 2, 8 read the partner through DPP (quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_ror:8, all inside a 16-lane row, hence inside
+// the team); M = 4 fetches it with ds_swizzle (bitmask mode, xor 4). The
+// DPP forms are written as inline assembly because the compiler does not
+// fold a DPP move into v_fmac; the leading s_nop 1 provides the two wait
+// states a DPP read needs after a VALU write of its source register (the
+// eight registers of one block are distinct, so no hazard arises inside).
+#define TQ_FMAC_DPP(k, ctrl) "v_fmac_f32_dpp %" #k ", %" #k ", %8 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define TQ_FMAC_DPP8(ctrl)                                                                                    \
+    "s_nop 1\n\t" TQ_FMAC_DPP(0, ctrl) TQ_FMAC_DPP(1, ctrl) TQ_FMAC_DPP(2, ctrl) TQ_FMAC_DPP(3, ctrl)            \
+        TQ_FMAC_DPP(4, ctrl) TQ_FMAC_DPP(5, ctrl) TQ_FMAC_DPP(6, ctrl) TQ_FMAC_DPP(7, ctrl)
+
+template <int M> __device__ __forceinline__ void fwht_cross(float (&y)[kGroup], float sigma)
 {
-    const uint32_t neg = (g & M) ? 0x80000000u : 0u;
+    if constexpr (M == 4) {
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-        const float own = as_f(as_u(y[j]) ^ neg);
-        y[j] = lane_xor<M>(y[j]) + own;
+        for (int j = 0; j < kGroup; ++j) {
+            const float p = as_f((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_u(y[j]), 0x101F));
+            y[j] = __builtin_fmaf(p, sigma, y[j]);
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < kGroup; b += 8) {
+            if constexpr (M == 1) {
+                asm volatile(TQ_FMAC_DPP8("quad_perm:[1,0,3,2]")
+                             : "+v"(y[b]), "+v"(y[b + 1]), "+v"(y[b + 2]), "+v"(y[b + 3]), "+v"(y[b + 4]),
+                               "+v"(y[b + 5]), "+v"(y[b + 6]), "+v"(y[b + 7])
+                             : "v"(sigma));
+            } else if constexpr (M == 2) {
+                asm volatile(TQ_FMAC_DPP8("quad_perm:[2,3,0,1]")
+                             : "+v"(y[b]), "+v"(y[b + 1]), "+v"(y[b + 2]), "+v"(y[b + 3]), "+v"(y[b + 4]),
+                               "+v"(y[b + 5]), "+v"(y[b + 6]), "+v"(y[b + 7])
+                             : "v"(sigma));
+            } else {
+                static_assert(M == 8, "cross-lane span");
+                asm volatile(TQ_FMAC_DPP8("row_ror:8")
+                             : "+v"(y[b]), "+v"(y[b + 1]), "+v"(y[b + 2]), "+v"(y[b + 3]), "+v"(y[b + 4]),
+                               "+v"(y[b + 5]), "+v"(y[b + 6]), "+v"(y[b + 7])
+                             : "v"(sigma));
+            }
+        }
     }
 }
 
-// normalised transform (butterflies of every span in increasing order,
-// then one multiply by binary32(1/sqrt(D)))
-template <int D> __device__ __forceinline__ void hadamard(float (&y)[kGroup], int g)
+// Per-lane constants of the transform for group g of a D-wide row.
+template <int D> struct Rot {
+    float sig1, sig2, sig4, sig8; // +1 in the lower group of each span, -1 in the upper one
+    float scale;                  // (-1)^popcount(g) * binary32(1/sqrt(D))
+    __device__ __forceinline__ explicit Rot(int g)
+    {
+        sig1 = (g & 1) ? -1.0f : 1.0f;
+        sig2 = (g & 2) ? -1.0f : 1.0f;
+        sig4 = (g & 4) ? -1.0f : 1.0f;
+        sig8 = (g & 8) ? -1.0f : 1.0f;
+        scale = (__builtin_popcount((unsigned)g & (D / kGroup - 1)) & 1) ? -HadScale<D>::v : HadScale<D>::v;
+    }
+};
+
+// normalised transform: butterflies of every span in increasing order, then
+// one multiply by binary32(1/sqrt(D)) (which also removes the carried sign)
+template <int D> __device__ __forceinline__ void hadamard(float (&y)[kGroup], const Rot<D> &rt)
 {
     fwht_in_lane(y);
-    if constexpr (D >= 64) fwht_cross<1>(y, g);
-    if constexpr (D >= 128) fwht_cross<2>(y, g);
-    if constexpr (D >= 256) fwht_cross<4>(y, g);
-    if constexpr (D >= 512) fwht_cross<8>(y, g);
-    const float r = HadScale<D>::v;
+    if constexpr (D >= 64) fwht_cross<1>(y, rt.sig1);
+    if constexpr (D >= 128) fwht_cross<2>(y, rt.sig2);
+    if constexpr (D >= 256) fwht_cross<4>(y, rt.sig4);
+    if constexpr (D >= 512) fwht_cross<8>(y, rt.sig8);
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) y[j] = y[j] * r;
+    for (int j = 0; j < kGroup; ++j) y[j] = y[j] * rt.scale;
 }
 
 // ---------------------------------------------------------------------------
 // Bin search and bit packing
 // ---------------------------------------------------------------------------
 
+// Number of boundaries strictly below z: base of z's cell plus one if z is
+// above the cell's boundary. bin_index_any accepts any z (infinities and
+// NaN included; NaN lands in cell 0) and is what the host evaluation runs;
+// bin_index_bounded needs |z| <= 6 and no NaN, which holds for every value
+// of a group whose sum of squares is finite.
 template <int B>
-__host__ __device__ __forceinline__ uint32_t bin_index(float z, const BinCell *lut)
+__host__ __device__ __forceinline__ uint32_t bin_index_any(float z, const BinCell *lut)
 {
     using Gr = BinGrid<B>;
-    float t = __builtin_fmaf(z, Gr::A, Gr::C);
-#if defined(__HIP_DEVICE_COMPILE__)
-    t = __builtin_amdgcn_fmed3f(t, 0.0f, (float)(Gr::N - 1));
-#else
-    t = fminf(fmaxf(t, 0.0f), (float)(Gr::N - 1));
-#endif
+    const float zc = fminf(fmaxf(z, -3.0e38f), 3.0e38f);
+    const float t = fminf(fmaxf(rintf(__builtin_fmaf(zc, Gr::A, Gr::C)), 0.0f), (float)(Gr::N - 1));
     const BinCell e = lut[(uint32_t)t];
+    return e.base + (zc > e.bnd ? 1u : 0u);
+}
+
+template <int B>
+__host__ __device__ __forceinline__ uint32_t bin_index_bounded(float z, const BinCell *lut)
+{
+    using Gr = BinGrid<B>;
+    const float t = __builtin_fmaf(z, Gr::A, Gr::C_MAGIC);
+    // bits(t) = bits(2^23) + cell; byte address = 8 * cell
+    const uint32_t addr = (__builtin_bit_cast(uint32_t, t) << 3) - (0x4B000000u << 3);
+    const BinCell e = *reinterpret_cast<const BinCell *>(reinterpret_cast<const char *>(lut) + addr);
     return e.base + (z > e.bnd ? 1u : 0u);
 }
 
-// 32 codes of B bits -> B dwords, element j at bits [j*B, j*B+B)
+// 32 codes of B bits -> B dwords, element j at bits [j*B, j*B+B). Codes
+// must be below 2^B, except for B == 8 where only the low byte of each
+// value is used (signed codes arrive as negative integers).
 template <int B> __device__ __forceinline__ void pack32(const uint32_t (&q)[kGroup], uint32_t (&w)[B])
 {
+    if constexpr (B == 8) {
 #pragma unroll
-    for (int k = 0; k < B; ++k) w[k] = 0;
+        for (int k = 0; k < 8; ++k) {
+            // v_perm_b32 selector bytes: 4 = byte 0 of the first operand, 0 = byte 0 of the second
+            const uint32_t lo = __builtin_amdgcn_perm(q[4 * k + 1], q[4 * k], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(q[4 * k + 3], q[4 * k + 2], 0x0c0c0400u);
+            w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+    } else {
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-        const int pos = j * B, k = pos >> 5, s = pos & 31;
-        w[k] |= q[j] << s;
-        if (s + B > 32) w[k + 1] |= q[j] >> (32 - s);
+        for (int k = 0; k < B; ++k) w[k] = 0;
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+            const int pos = j * B, k = pos >> 5, s = pos & 31;
+            w[k] |= q[j] << s;
+            if (s + B > 32) w[k + 1] |= q[j] >> (32 - s);
+        }
     }
 }
 
@@ -352,70 +438,59 @@ template <int B> __device__ __forceinline__ void load_codes(const uint8_t *p, ui
 // Group loads and stores (32 elements, 16-byte vectors)
 // ---------------------------------------------------------------------------
 
-// load a group and multiply by the signs when `smask` is not zero
-template <bool BF16>
-__device__ __forceinline__ void load_group(const void *base, int64_t e0, uint32_t smask, float (&x)[kGroup])
-{
-    if constexpr (BF16) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + e0);
-        uint32_t w[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 a = p[i];
-            w[4 * i + 0] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t u = w[k] ^ sign_pair_mask(smask, k);
-            x[2 * k] = as_f(u << 16);
-            x[2 * k + 1] = as_f(u & 0xffff0000u);
-        }
-    } else {
-        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + e0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 a = p[i];
-            x[4 * i + 0] = a.x; x[4 * i + 1] = a.y; x[4 * i + 2] = a.z; x[4 * i + 3] = a.w;
-        }
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) x[j] = as_f(as_u(x[j]) ^ (((smask >> j) & 1u) << 31));
-    }
-}
-
-// store a group, multiplying by the signs given by `smask` (0: none)
-template <bool BF16>
-__device__ __forceinline__ void store_group(void *base, int64_t e0, uint32_t smask, const float (&y)[kGroup])
-{
-    if constexpr (BF16) {
-        uint4 *p = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(base) + e0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t w[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int k = 4 * i + t;
-                w[t] = pack_bf16x2(y[2 * k], y[2 * k + 1]) ^ sign_pair_mask(smask, k);
-            }
-            p[i] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    } else {
-        float4 *p = reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + e0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float v[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int j = 4 * i + t;
-                v[t] = as_f(as_u(y[j]) ^ (((smask >> j) & 1u) << 31));
-            }
-            p[i] = make_float4(v[0], v[1], v[2], v[3]);
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Key path (per lane, no communication)
 // ---------------------------------------------------------------------------
+
+// Minimum and maximum of a group, equal to a scan with strict comparisons
+// that keeps the first of equal values. v_min3/v_max3 give the extreme
+// values (two new elements per instruction; inline assembly because the
+// compiler would first canonicalise every operand loaded as raw bits); only
+// the sign of a zero extreme can differ from the scan's, so when an extreme
+// is zero it is replaced by the first element equal to zero.
+__device__ __forceinline__ float min3f(float a, float b, float c)
+{
+    float r;
+    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ void group_min_max(const float (&x)[kGroup], float &mn, float &mx)
+{
+    float a = min3f(x[0], x[1], x[2]);
+    float b = max3f(x[0], x[1], x[2]);
+#pragma unroll
+    for (int j = 3; j < kGroup; j += 2) {
+        if (j + 1 < kGroup) {
+            a = min3f(a, x[j], x[j + 1]);
+            b = max3f(b, x[j], x[j + 1]);
+        } else {
+            a = min3f(a, x[j], x[j]);
+            b = max3f(b, x[j], x[j]);
+        }
+    }
+    if (a == 0.0f || b == 0.0f) {
+        float first_zero = 0.0f;
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+            const bool z = !found && x[j] == 0.0f;
+            first_zero = z ? x[j] : first_zero;
+            found = found || z;
+        }
+        if (a == 0.0f) a = first_zero;
+        if (b == 0.0f) b = first_zero;
+    }
+    mn = a;
+    mx = b;
+}
 
 // quotient a / b rounded to nearest, from r = RN(1/b) (see file header)
 __device__ __forceinline__ float quot(float a, float b, float r)
@@ -429,14 +504,8 @@ template <int KB, bool KS>
 __device__ __forceinline__ void key_encode_group(const float (&x)[kGroup], uint8_t *codes,
                                                  uint16_t *scale_out, uint16_t *zero_out)
 {
-    // sequential min / max, keeping the first of equal values (as a scan
-    // with strict comparisons does)
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int j = 1; j < kGroup; ++j) {
-        mn = (x[j] < mn) ? x[j] : mn;
-        mx = (x[j] > mx) ? x[j] : mx;
-    }
+    float mn, mx;
+    group_min_max(x, mn, mx);
     const float eps = 1e-8f;
     constexpr int maxv = KS ? 127 : (1 << KB) - 1;
     float scale, zp;
@@ -460,14 +529,14 @@ __device__ __forceinline__ void key_encode_group(const float (&x)[kGroup], uint8
         for (int j = 0; j < kGroup; ++j) {
             const float o = quot(x[j], se, r);
             const float c = __builtin_amdgcn_fmed3f(rintf(o - zp), lo, hi);
-            q[j] = (uint32_t)(int32_t)c & 0xffu;
+            q[j] = (uint32_t)(int32_t)c;
         }
     } else {
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) {
             const float o = x[j] / se;
             const float c = __builtin_amdgcn_fmed3f(rintf(o - zp), lo, hi);
-            q[j] = (uint32_t)(int32_t)c & 0xffu;
+            q[j] = (uint32_t)(int32_t)c;
         }
     }
     uint32_t w[KB];
@@ -477,23 +546,81 @@ __device__ __forceinline__ void key_encode_group(const float (&x)[kGroup], uint8
     *zero_out = f32_to_f16_bits(zp);
 }
 
-template <int KB, bool KS, bool BF16>
-__device__ __forceinline__ void key_decode_group(const uint8_t *codes, uint16_t scale16, uint16_t zero16,
-                                                 void *out, int64_t e0)
+
+// ---------------------------------------------------------------------------
+// Coalesced output through LDS
+// ---------------------------------------------------------------------------
+
+// A wavefront's 64 lanes hold 64 consecutive 32-element groups, i.e. one
+// contiguous tile of the output (4 KB in bf16, 8 KB in f32), but each lane
+// owns a 64 B (128 B) piece of it. Written directly, every store
+// instruction would touch 64 pieces 64 B apart. Instead each lane writes its
+// piece to a per-wavefront LDS area (pieces padded by 16 B, which keeps the
+// 16-byte LDS accesses free of bank conflicts) and the wavefront then
+// stores the tile so that each instruction covers a contiguous 1 KB.
+template <bool BF16> struct Stage {
+    static constexpr int CH = BF16 ? 4 : 8;   // 16-byte chunks per lane
+    static constexpr int STRIDE = CH + 1;     // padded piece, in 16-byte units
+    static constexpr int LPI = kWave / CH;    // pieces covered by one store instruction
+    static constexpr int WORDS = kWave * STRIDE;
+};
+
+__device__ __forceinline__ void wave_lds_sync()
 {
-    uint32_t w[KB];
-    load_codes<KB>(codes, w);
-    const float scale = f16_bits_to_f32(scale16);
-    const float zero = f16_bits_to_f32(zero16);
-    float y[kGroup];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Store the tile whose first row is row0 (rows_per_wave rows of D elements),
+// converting to the output type and flipping signs per `smask`; rows at or
+// beyond `rows` are not written.
+template <int D, bool BF16>
+__device__ __forceinline__ void store_tile(void *base, int64_t row0, int64_t rows, uint32_t smask,
+                                           const float (&y)[kGroup], uint4 *stage)
+{
+    using S = Stage<BF16>;
+    constexpr int G = D / kGroup;
+    const int lane = threadIdx.x & (kWave - 1);
+    uint4 w[S::CH];
+    if constexpr (BF16) {
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-        const uint32_t u = unpack1<KB>(w, j);
-        const float qf = KS ? (float)(int32_t)(int8_t)(uint8_t)u : (float)u;
-        const float s = qf + zero;
-        y[j] = s * scale;
+        for (int i = 0; i < 4; ++i) {
+            uint32_t q[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = 4 * i + t;
+                q[t] = pack_bf16x2(y[2 * k], y[2 * k + 1]) ^ sign_pair_mask(smask, k);
+            }
+            w[i] = make_uint4(q[0], q[1], q[2], q[3]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t q[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int j = 4 * i + t;
+                q[t] = as_u(y[j]) ^ (((smask >> j) & 1u) << 31);
+            }
+            w[i] = make_uint4(q[0], q[1], q[2], q[3]);
+        }
     }
-    store_group<BF16>(out, e0, 0u, y);
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < S::CH; ++i) stage[lane * S::STRIDE + i] = w[i];
+    wave_lds_sync();
+    constexpr int elem_bytes = BF16 ? 2 : 4;
+    uint8_t *tile = reinterpret_cast<uint8_t *>(base) + row0 * (int64_t)(D * elem_bytes);
+    const int c_lo = lane % S::LPI;
+    const int sub = lane / S::LPI;
+#pragma unroll
+    for (int i = 0; i < S::CH; ++i) {
+        const int c = S::LPI * i + c_lo;               // piece = writer lane
+        const uint4 v = stage[c * S::STRIDE + sub];
+        if (row0 + c / G < rows)
+            *reinterpret_cast<uint4 *>(tile + (c * S::CH + sub) * 16) = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -503,55 +630,104 @@ __device__ __forceinline__ void key_decode_group(const uint8_t *codes, uint16_t 
 // key modes: bits | (signed << 4); 0 = no key side
 enum { KMODE_NONE = 0 };
 
-template <int D, int VB, bool BF16IN>
-__global__ void __launch_bounds__(kBlockThreads)
-encode_kernel(const void *__restrict__ kin, const void *__restrict__ vin, int64_t rows, int32_t kmode,
-              uint8_t *__restrict__ kc, uint16_t *__restrict__ ks, uint16_t *__restrict__ kz,
-              uint8_t *__restrict__ vc, uint16_t *__restrict__ vs)
+// One group as loaded: 32 elements in 16-byte vectors.
+template <bool BF16> struct RawGroup {
+    uint4 v[BF16 ? 4 : 8];
+};
+
+template <bool BF16> __device__ __forceinline__ void load_raw(const void *base, int64_t e0, RawGroup<BF16> &r)
+{
+    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(base) + e0 * (BF16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < (BF16 ? 4 : 8); ++i) r.v[i] = p[i];
+}
+
+// binary32 values of a raw group, multiplied by the signs in `smask`
+template <bool BF16>
+__device__ __forceinline__ void raw_to_f32(const RawGroup<BF16> &r, uint32_t smask, float (&x)[kGroup])
+{
+    if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = 4 * i + t;
+                const uint32_t u = w[t] ^ sign_pair_mask(smask, k);
+                x[2 * k] = as_f(u << 16);
+                x[2 * k + 1] = as_f(u & 0xffff0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int j = 4 * i + t;
+                x[j] = as_f(w[t] ^ (((smask >> j) & 1u) << 31));
+            }
+        }
+    }
+}
+
+// Tile loop of the encoder for one key mode (KB = 0: values only). A
+// wavefront walks tiles t, t + stride, ...; the key input of the next tile
+// is loaded while the current tile's values are processed.
+template <int D, int VB, int KB, bool KS, bool BF16IN>
+__device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const void *__restrict__ vin, int64_t rows,
+                                            uint8_t *__restrict__ kc, uint16_t *__restrict__ ks,
+                                            uint16_t *__restrict__ kz, uint8_t *__restrict__ vc,
+                                            uint16_t *__restrict__ vs, const BinCell *lut)
 {
     constexpr int G = D / kGroup;
     constexpr int RPW = kWave / G;
-    constexpr int NCELL = BinGrid<VB>::N;
-    __shared__ BinCell lut[NCELL];
-    if (vin != nullptr) {
-        const BinCell *src = dev_lut<VB>();
-        for (int i = threadIdx.x; i < NCELL; i += kBlockThreads) lut[i] = src[i];
-        __syncthreads();
-    }
+    constexpr bool HASK = KB != 0;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int g = lane % G;
     const int rl = lane / G;
     const uint32_t smask = dev_sign<D>(g);
+    const Rot<D> rot(g);
+    const bool hasv = vin != nullptr;
     const int64_t tiles = (rows + RPW - 1) / RPW;
-    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave; t < tiles;
-         t += (int64_t)gridDim.x * kWavesPerBlock) {
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+    int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    constexpr bool PREFETCH = HASK && TQ_ENCODE_PREFETCH_K;
+    RawGroup<BF16IN> kraw;
+    if constexpr (PREFETCH) {
+        const int64_t row = t * RPW + rl;
+        if (t < tiles && row < rows) load_raw<BF16IN>(kin, row * D + (int64_t)g * kGroup, kraw);
+    }
+    for (; t < tiles; t += stride) {
         const int64_t row = t * RPW + rl;
         const bool act = row < rows;
         const int64_t e0 = row * D + (int64_t)g * kGroup;
         const int64_t grp = row * G + g;
-        if (kmode != KMODE_NONE && act) {
-            float x[kGroup];
-            load_group<BF16IN>(kin, e0, 0u, x);
-            switch (kmode) {
-            case 2: key_encode_group<2, false>(x, kc + grp * 8, ks + grp, kz + grp); break;
-            case 3: key_encode_group<3, false>(x, kc + grp * 12, ks + grp, kz + grp); break;
-            case 4: key_encode_group<4, false>(x, kc + grp * 16, ks + grp, kz + grp); break;
-            case 5: key_encode_group<5, false>(x, kc + grp * 20, ks + grp, kz + grp); break;
-            case 8: key_encode_group<8, false>(x, kc + grp * 32, ks + grp, kz + grp); break;
-            case 8 | 16: key_encode_group<8, true>(x, kc + grp * 32, ks + grp, kz + grp); break;
-            default: break;
+        RawGroup<BF16IN> vraw;
+        if (hasv && act) load_raw<BF16IN>(vin, e0, vraw);
+        if constexpr (HASK) {
+            if (act) {
+                if constexpr (!PREFETCH) load_raw<BF16IN>(kin, e0, kraw);
+                float x[kGroup];
+                raw_to_f32<BF16IN>(kraw, 0u, x);
+                key_encode_group<KB, KS>(x, kc + grp * (4 * KB), ks + grp, kz + grp);
+            }
+            if constexpr (PREFETCH) {
+                const int64_t tn = t + stride;
+                const int64_t rown = tn * RPW + rl;
+                if (tn < tiles && rown < rows) load_raw<BF16IN>(kin, rown * D + (int64_t)g * kGroup, kraw);
             }
         }
-        if (vin != nullptr) {
+        if (hasv) {
             float y[kGroup];
             if (act) {
-                load_group<BF16IN>(vin, e0, smask, y);
+                raw_to_f32<BF16IN>(vraw, smask, y);
             } else {
 #pragma unroll
                 for (int j = 0; j < kGroup; ++j) y[j] = 0.0f;
             }
-            hadamard<D>(y, g);
+            hadamard<D>(y, rot);
             float ss = 0.0f;
 #pragma unroll
             for (int j = 0; j < kGroup; ++j) {
@@ -563,11 +739,12 @@ encode_kernel(const void *__restrict__ kin, const void *__restrict__ vin, int64_
             const float r = 1.0f / se;
             uint32_t q[kGroup];
             if (se < 1e30f) {
+                // ss finite: every y finite and |y / se| <= sqrt(32)
 #pragma unroll
-                for (int j = 0; j < kGroup; ++j) q[j] = bin_index<VB>(quot(y[j], se, r), lut);
+                for (int j = 0; j < kGroup; ++j) q[j] = bin_index_bounded<VB>(quot(y[j], se, r), lut);
             } else {
 #pragma unroll
-                for (int j = 0; j < kGroup; ++j) q[j] = bin_index<VB>(y[j] / se, lut);
+                for (int j = 0; j < kGroup; ++j) q[j] = bin_index_any<VB>(y[j] / se, lut);
             }
             if (act) {
                 uint32_t w[VB];
@@ -579,91 +756,192 @@ encode_kernel(const void *__restrict__ kin, const void *__restrict__ vin, int64_
     }
 }
 
+#if TQ_ENCODE_WAVES > 0
+#define TQ_ENCODE_ATTR __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(TQ_ENCODE_WAVES)))
+#else
+#define TQ_ENCODE_ATTR __launch_bounds__(kBlockThreads)
+#endif
+
+template <int D, int VB, bool BF16IN>
+__global__ void TQ_ENCODE_ATTR
+encode_kernel(const void *__restrict__ kin, const void *__restrict__ vin, int64_t rows, int32_t kmode,
+              uint8_t *__restrict__ kc, uint16_t *__restrict__ ks, uint16_t *__restrict__ kz,
+              uint8_t *__restrict__ vc, uint16_t *__restrict__ vs)
+{
+    constexpr int NCELL = BinGrid<VB>::N;
+    __shared__ BinCell lut[NCELL];
+    if (vin != nullptr) {
+        const BinCell *src = dev_lut<VB>();
+        for (int i = threadIdx.x; i < NCELL; i += kBlockThreads) lut[i] = src[i];
+        __syncthreads();
+    }
+    switch (kmode) {
+    case 2: encode_loop<D, VB, 2, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
+    case 3: encode_loop<D, VB, 3, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
+    case 4: encode_loop<D, VB, 4, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
+    case 5: encode_loop<D, VB, 5, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
+    case 8: encode_loop<D, VB, 8, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
+    case 8 | 16: encode_loop<D, VB, 8, true, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
+    default: encode_loop<D, VB, 0, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
+    }
+}
+
+// Packed input of one group for the decoder: code words and fp16 bits.
+template <int KB, int VB> struct GroupCodes {
+    uint32_t kw[KB > 0 ? KB : 1];
+    uint32_t vw[VB];
+    uint32_t ks, kz, vs;
+};
+
+template <int D, int VB, int KB>
+__device__ __forceinline__ void load_group_codes(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks,
+                                                 const uint16_t *__restrict__ kz, const uint8_t *__restrict__ vc,
+                                                 const uint16_t *__restrict__ vs, int64_t row, int64_t rows, int g,
+                                                 bool hasv, GroupCodes<KB, VB> &c)
+{
+    constexpr int G = D / kGroup;
+    const int64_t grp = row * G + g;
+#pragma unroll
+    for (int k = 0; k < (KB > 0 ? KB : 1); ++k) c.kw[k] = 0;
+#pragma unroll
+    for (int k = 0; k < VB; ++k) c.vw[k] = 0;
+    c.ks = c.kz = c.vs = 0;
+    if (row < rows) {
+        if constexpr (KB != 0) {
+            load_codes<KB>(kc + grp * (4 * KB), c.kw);
+            c.ks = ks[grp];
+            c.kz = kz[grp];
+        }
+        if (hasv) {
+            load_codes<VB>(vc + grp * (4 * VB), c.vw);
+            c.vs = vs[grp];
+        }
+    }
+}
+
+// Tile loop of the decoder for one key mode (KB = 0: values only). The
+// codes of the next tile are loaded before the current tile is decoded.
+template <int D, int VB, int KB, bool KS, bool BF16OUT>
+__device__ __forceinline__ void decode_loop(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks,
+                                            const uint16_t *__restrict__ kz, const uint8_t *__restrict__ vc,
+                                            const uint16_t *__restrict__ vs, int64_t rows, int32_t rotated,
+                                            void *__restrict__ kout, void *__restrict__ vout, const float *cent,
+                                            uint4 *stage)
+{
+    constexpr int G = D / kGroup;
+    constexpr int RPW = kWave / G;
+    constexpr bool HASK = KB != 0;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int g = lane % G;
+    const int rl = lane / G;
+    const uint32_t smask = rotated ? 0u : dev_sign<D>(g);
+    const Rot<D> rot(g);
+    const bool hasv = vout != nullptr;
+    const int64_t tiles = (rows + RPW - 1) / RPW;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+
+    int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    GroupCodes<KB, VB> cur;
+    load_group_codes<D, VB, KB>(kc, ks, kz, vc, vs, t < tiles ? t * RPW + rl : rows, rows, g, hasv, cur);
+    for (; t < tiles; t += stride) {
+        const int64_t tn = t + stride;
+        GroupCodes<KB, VB> nxt;
+        load_group_codes<D, VB, KB>(kc, ks, kz, vc, vs, tn < tiles ? tn * RPW + rl : rows, rows, g, hasv, nxt);
+        const int64_t row0 = t * RPW;
+        if constexpr (HASK) {
+            float y[kGroup];
+            const float scale = f16_bits_to_f32((uint16_t)cur.ks);
+            const float zero = f16_bits_to_f32((uint16_t)cur.kz);
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                const uint32_t u = unpack1<KB>(cur.kw, j);
+                const float qf = KS ? (float)(int32_t)(int8_t)(uint8_t)u : (float)u;
+                const float sum = qf + zero;
+                y[j] = sum * scale;
+            }
+            store_tile<D, BF16OUT>(kout, row0, rows, 0u, y, stage);
+        }
+        if (hasv) {
+            float y[kGroup];
+            const float s = f16_bits_to_f32((uint16_t)cur.vs);
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) y[j] = cent[unpack1<VB>(cur.vw, j)] * s;
+            if (!rotated) hadamard<D>(y, rot);
+            store_tile<D, BF16OUT>(vout, row0, rows, smask, y, stage);
+        }
+#pragma unroll
+        for (int k = 0; k < (KB > 0 ? KB : 1); ++k) cur.kw[k] = nxt.kw[k];
+#pragma unroll
+        for (int k = 0; k < VB; ++k) cur.vw[k] = nxt.vw[k];
+        cur.ks = nxt.ks;
+        cur.kz = nxt.kz;
+        cur.vs = nxt.vs;
+    }
+}
+
 template <int D, int VB, bool BF16OUT>
 __global__ void __launch_bounds__(kBlockThreads)
 decode_kernel(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks, const uint16_t *__restrict__ kz,
               const uint8_t *__restrict__ vc, const uint16_t *__restrict__ vs, int64_t rows, int32_t kmode,
               int32_t rotated, void *__restrict__ kout, void *__restrict__ vout)
 {
-    constexpr int G = D / kGroup;
-    constexpr int RPW = kWave / G;
     constexpr int NC = 1 << VB;
+    using S = Stage<BF16OUT>;
     __shared__ float cent[NC];
+    __shared__ uint4 stage_all[kWavesPerBlock * S::WORDS];
     if (vout != nullptr) {
         const float *src = dev_cent<VB>();
         for (int i = threadIdx.x; i < NC; i += kBlockThreads) cent[i] = src[i];
         __syncthreads();
     }
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int g = lane % G;
-    const int rl = lane / G;
-    const uint32_t smask = rotated ? 0u : dev_sign<D>(g);
-    const int64_t tiles = (rows + RPW - 1) / RPW;
-    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave; t < tiles;
-         t += (int64_t)gridDim.x * kWavesPerBlock) {
-        const int64_t row = t * RPW + rl;
-        const bool act = row < rows;
-        const int64_t e0 = row * D + (int64_t)g * kGroup;
-        const int64_t grp = row * G + g;
-        if (kmode != KMODE_NONE && act) {
-            const uint16_t s16 = ks[grp], z16 = kz[grp];
-            switch (kmode) {
-            case 2: key_decode_group<2, false, BF16OUT>(kc + grp * 8, s16, z16, kout, e0); break;
-            case 3: key_decode_group<3, false, BF16OUT>(kc + grp * 12, s16, z16, kout, e0); break;
-            case 4: key_decode_group<4, false, BF16OUT>(kc + grp * 16, s16, z16, kout, e0); break;
-            case 5: key_decode_group<5, false, BF16OUT>(kc + grp * 20, s16, z16, kout, e0); break;
-            case 8: key_decode_group<8, false, BF16OUT>(kc + grp * 32, s16, z16, kout, e0); break;
-            case 8 | 16: key_decode_group<8, true, BF16OUT>(kc + grp * 32, s16, z16, kout, e0); break;
-            default: break;
-            }
-        }
-        if (vout != nullptr) {
-            float y[kGroup];
-            uint32_t w[VB];
-            float s = 0.0f;
-            if (act) {
-                load_codes<VB>(vc + grp * (4 * VB), w);
-                s = f16_bits_to_f32(vs[grp]);
-            } else {
-#pragma unroll
-                for (int k = 0; k < VB; ++k) w[k] = 0;
-            }
-#pragma unroll
-            for (int j = 0; j < kGroup; ++j) y[j] = cent[unpack1<VB>(w, j)] * s;
-            if (!rotated) hadamard<D>(y, g);
-            if (act) store_group<BF16OUT>(vout, e0, smask, y);
-        }
+    uint4 *stage = stage_all + (threadIdx.x / kWave) * S::WORDS;
+    switch (kmode) {
+    case 2: decode_loop<D, VB, 2, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
+    case 3: decode_loop<D, VB, 3, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
+    case 4: decode_loop<D, VB, 4, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
+    case 5: decode_loop<D, VB, 5, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
+    case 8: decode_loop<D, VB, 8, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
+    case 8 | 16: decode_loop<D, VB, 8, true, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
+    default: decode_loop<D, VB, 0, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
     }
 }
 
-// inverse rotation of attention outputs (rows of D elements, f32 or bf16)
+// inverse rotation of attention outputs (rows of D elements, f32 or bf16);
+// x and out may be the same buffer
 template <int D, bool BF16>
 __global__ void __launch_bounds__(kBlockThreads)
-unrotate_kernel(const void *__restrict__ x, void *__restrict__ out, int64_t rows)
+unrotate_kernel(const void *x, void *out, int64_t rows)
 {
     constexpr int G = D / kGroup;
     constexpr int RPW = kWave / G;
+    using S = Stage<BF16>;
+    __shared__ uint4 stage_all[kWavesPerBlock * S::WORDS];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    uint4 *stage = stage_all + wave * S::WORDS;
     const int g = lane % G;
     const int rl = lane / G;
     const uint32_t smask = dev_sign<D>(g);
+    const Rot<D> rot(g);
     const int64_t tiles = (rows + RPW - 1) / RPW;
     for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave; t < tiles;
          t += (int64_t)gridDim.x * kWavesPerBlock) {
-        const int64_t row = t * RPW + rl;
+        const int64_t row0 = t * RPW;
+        const int64_t row = row0 + rl;
         const bool act = row < rows;
         const int64_t e0 = row * D + (int64_t)g * kGroup;
         float y[kGroup];
         if (act) {
-            load_group<BF16>(x, e0, 0u, y);
+            RawGroup<BF16> raw;
+            load_raw<BF16>(x, e0, raw);
+            raw_to_f32<BF16>(raw, 0u, y);
         } else {
 #pragma unroll
             for (int j = 0; j < kGroup; ++j) y[j] = 0.0f;
         }
-        hadamard<D>(y, g);
-        if (act) store_group<BF16>(out, e0, smask, y);
+        hadamard<D>(y, rot);
+        store_tile<D, BF16>(out, row0, rows, smask, y, stage);
     }
 }
 
@@ -676,12 +954,44 @@ bool valid_bits(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 5 || b ==
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 uintptr_t code_align(int32_t bits) { return (bits == 4 || bits == 8) ? 16 : 8; }
 
-int64_t grid_for(int64_t rows, int32_t d)
+// Persistent grid: as many blocks as can be resident at once (occupancy of
+// the kernel times the device's compute units), capped by the number of
+// tiles. TQ_BLOCKS_PER_CU, if set, replaces the occupancy figure (for
+// tuning sweeps).
+int64_t grid_for(const void *fn, int64_t rows, int32_t d)
 {
+    static std::mutex mu;
+    static std::unordered_map<const void *, int> occupancy;
+    static int cus[64] = {0};
+    static int env_per_cu = -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int per_cu = 0, ncu = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (env_per_cu < 0) {
+            const char *e = getenv("TQ_BLOCKS_PER_CU");
+            env_per_cu = (e != nullptr && atoi(e) > 0) ? atoi(e) : 0;
+        }
+        if (cus[dev] == 0) {
+            int n = 0;
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+            cus[dev] = n;
+        }
+        ncu = cus[dev];
+        auto it = occupancy.find(fn);
+        if (it == occupancy.end()) {
+            int b = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, kBlockThreads, 0) != hipSuccess || b <= 0) b = 2;
+            it = occupancy.emplace(fn, b).first;
+        }
+        per_cu = env_per_cu > 0 ? env_per_cu : it->second;
+    }
     const int64_t rpw = kWave / (d / kGroup);
     const int64_t tiles = (rows + rpw - 1) / rpw;
     int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+    const int64_t resident = (int64_t)per_cu * ncu;
+    if (blocks > resident) blocks = resident;
     return blocks < 1 ? 1 : blocks;
 }
 
@@ -798,9 +1108,13 @@ int32_t tq_encode_kv(const void *k, const void *v, int32_t in_dtype, int64_t tok
                      const tq_config *cfg, const tq_packed_kv *out, void *stream)
 {
     if (cfg == nullptr || out == nullptr) return TQ_E_NULL;
-    if (k == nullptr && v == nullptr) return TQ_E_NULL;
     if (!valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
     if (in_dtype != TQ_F32 && in_dtype != TQ_BF16) return TQ_E_DTYPE;
+    int64_t rows = 0;
+    const int32_t st = check_rows(tokens, heads, &rows);
+    if (st != TQ_OK) return st;
+    if (rows == 0) return TQ_OK;
+    if (k == nullptr && v == nullptr) return TQ_E_NULL;
     if (k != nullptr) {
         if (!valid_bits(cfg->k_bits) || (cfg->k_signed != 0 && cfg->k_bits != 8) ||
             (cfg->k_signed != 0 && cfg->k_signed != 1))
@@ -816,14 +1130,10 @@ int32_t tq_encode_kv(const void *k, const void *v, int32_t in_dtype, int64_t tok
         if (!aligned(v, 16) || !aligned(out->v_codes, code_align(cfg->v_bits)) || !aligned(out->v_scale, 2))
             return TQ_E_ALIGN;
     }
-    int64_t rows = 0;
-    const int32_t st = check_rows(tokens, heads, &rows);
-    if (st != TQ_OK) return st;
-    if (rows == 0) return TQ_OK;
     const int32_t vb = (v != nullptr) ? cfg->v_bits : 4;
     EncodeFn fn = (in_dtype == TQ_BF16) ? pick_encode<true>(cfg->head_dim, vb) : pick_encode<false>(cfg->head_dim, vb);
     const int32_t kmode = (k != nullptr) ? key_mode(cfg) : KMODE_NONE;
-    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for(rows, cfg->head_dim)), dim3(kBlockThreads), 0,
+    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for((const void *)fn, rows, cfg->head_dim)), dim3(kBlockThreads), 0,
                        (hipStream_t)stream, k, v, rows, kmode, (uint8_t *)out->k_codes, (uint16_t *)out->k_scale,
                        (uint16_t *)out->k_zero, (uint8_t *)out->v_codes, (uint16_t *)out->v_scale);
     return launch_status();
@@ -833,10 +1143,14 @@ int32_t tq_decode_kv(const tq_packed_kv *in, int64_t tokens, int32_t heads, cons
                      void *v_out, int32_t out_dtype, int32_t flags, void *stream)
 {
     if (cfg == nullptr || in == nullptr) return TQ_E_NULL;
-    if (k_out == nullptr && v_out == nullptr) return TQ_E_NULL;
     if (!valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
     if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_E_DTYPE;
     if ((flags & ~TQ_DECODE_ROTATED_V) != 0) return TQ_E_SHAPE;
+    int64_t rows = 0;
+    const int32_t st = check_rows(tokens, heads, &rows);
+    if (st != TQ_OK) return st;
+    if (rows == 0) return TQ_OK;
+    if (k_out == nullptr && v_out == nullptr) return TQ_E_NULL;
     if (k_out != nullptr) {
         if (!valid_bits(cfg->k_bits) || (cfg->k_signed != 0 && cfg->k_bits != 8) ||
             (cfg->k_signed != 0 && cfg->k_signed != 1))
@@ -852,14 +1166,10 @@ int32_t tq_decode_kv(const tq_packed_kv *in, int64_t tokens, int32_t heads, cons
         if (!aligned(v_out, 16) || !aligned(in->v_codes, code_align(cfg->v_bits)) || !aligned(in->v_scale, 2))
             return TQ_E_ALIGN;
     }
-    int64_t rows = 0;
-    const int32_t st = check_rows(tokens, heads, &rows);
-    if (st != TQ_OK) return st;
-    if (rows == 0) return TQ_OK;
     const int32_t vb = (v_out != nullptr) ? cfg->v_bits : 4;
     DecodeFn fn = (out_dtype == TQ_BF16) ? pick_decode<true>(cfg->head_dim, vb) : pick_decode<false>(cfg->head_dim, vb);
     const int32_t kmode = (k_out != nullptr) ? key_mode(cfg) : KMODE_NONE;
-    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for(rows, cfg->head_dim)), dim3(kBlockThreads), 0,
+    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for((const void *)fn, rows, cfg->head_dim)), dim3(kBlockThreads), 0,
                        (hipStream_t)stream, (const uint8_t *)in->k_codes, (const uint16_t *)in->k_scale,
                        (const uint16_t *)in->k_zero, (const uint8_t *)in->v_codes, (const uint16_t *)in->v_scale,
                        rows, kmode, (int32_t)((flags & TQ_DECODE_ROTATED_V) != 0), k_out, v_out);
@@ -868,15 +1178,15 @@ int32_t tq_decode_kv(const tq_packed_kv *in, int64_t tokens, int32_t heads, cons
 
 int32_t tq_unrotate_values(const void *x, void *out, int32_t dtype, int64_t rows, int32_t head_dim, void *stream)
 {
-    if (x == nullptr || out == nullptr) return TQ_E_NULL;
     if (!valid_head_dim(head_dim)) return TQ_E_HEAD_DIM;
     if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_E_DTYPE;
     if (rows < 0 || rows > ((int64_t)1 << 44)) return TQ_E_SHAPE;
-    if (!aligned(x, 16) || !aligned(out, 16)) return TQ_E_ALIGN;
     if (rows == 0) return TQ_OK;
+    if (x == nullptr || out == nullptr) return TQ_E_NULL;
+    if (!aligned(x, 16) || !aligned(out, 16)) return TQ_E_ALIGN;
     UnrotateFn fn = (dtype == TQ_BF16) ? pick_unrotate<true>(head_dim) : pick_unrotate<false>(head_dim);
-    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for(rows, head_dim)), dim3(kBlockThreads), 0, (hipStream_t)stream, x,
-                       out, rows);
+    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for((const void *)fn, rows, head_dim)), dim3(kBlockThreads), 0,
+                       (hipStream_t)stream, x, out, rows);
     return launch_status();
 }
 
@@ -920,13 +1230,15 @@ int32_t tq_value_bin_host(int32_t bits, const float *z, int64_t n, uint8_t *idx)
     static constexpr BinLut<5> l5{};
     static constexpr BinLut<8> l8{};
     for (int64_t i = 0; i < n; ++i) {
+        // the kernels' fast path for |z| <= 6, the general path otherwise
+        const bool bounded = fabsf(z[i]) <= 6.0f;
         uint32_t r = 0;
         switch (bits) {
-        case 2: r = bin_index<2>(z[i], l2.cell); break;
-        case 3: r = bin_index<3>(z[i], l3.cell); break;
-        case 4: r = bin_index<4>(z[i], l4.cell); break;
-        case 5: r = bin_index<5>(z[i], l5.cell); break;
-        default: r = bin_index<8>(z[i], l8.cell); break;
+        case 2: r = bounded ? bin_index_bounded<2>(z[i], l2.cell) : bin_index_any<2>(z[i], l2.cell); break;
+        case 3: r = bounded ? bin_index_bounded<3>(z[i], l3.cell) : bin_index_any<3>(z[i], l3.cell); break;
+        case 4: r = bounded ? bin_index_bounded<4>(z[i], l4.cell) : bin_index_any<4>(z[i], l4.cell); break;
+        case 5: r = bounded ? bin_index_bounded<5>(z[i], l5.cell) : bin_index_any<5>(z[i], l5.cell); break;
+        default: r = bounded ? bin_index_bounded<8>(z[i], l8.cell) : bin_index_any<8>(z[i], l8.cell); break;
         }
         idx[i] = (uint8_t)r;
     }

@@ -1,0 +1,126 @@
+"""Summaries of rocprofv3 output for the codec kernels.
+
+    python -m kv_cache_quantization_tq_amd.profiling trace <kernel_trace.csv>
+    python -m kv_cache_quantization_tq_amd.profiling traffic <fetch.csv> <write.csv> \
+        --copy-mib 512 [--json out.json]
+
+``trace`` prints per-kernel dispatch counts and average / median / min
+durations from a ``--kernel-trace`` CSV. ``traffic`` turns the FETCH_SIZE and
+WRITE_SIZE counters (KiB per dispatch) of two ``--pmc`` runs of
+``bench.py --copy-calibration-mib N`` into HBM bytes per launch: each
+counter is scaled by the factor that maps the same counter, read on the
+plain device copy of N MiB in the same run, to its known N MiB.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "csrc", "tq_codec.hip")
+
+
+def kernel_kind(name: str) -> str:
+    if "encode_kernel" in name:
+        return "encode"
+    if "decode_kernel" in name:
+        return "decode"
+    if "unrotate_kernel" in name:
+        return "unrotate"
+    if "copyBuffer" in name:
+        return "copy"
+    return "other"
+
+
+def short_name(name: str) -> str:
+    m = re.search(r"(\w+_kernel<[^>]*>)", name)
+    return m.group(1) if m else name[:80]
+
+
+def read_trace(path: str):
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            out.setdefault(short_name(name), []).append(dur)
+    return out
+
+
+def trace_summary(path: str) -> str:
+    rows = []
+    for name, d in read_trace(path).items():
+        if kernel_kind(name) in ("encode", "decode", "unrotate"):
+            rows.append((name, len(d), sum(d) / len(d), statistics.median(d), min(d)))
+    lines = [f"{'kernel':70s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} {'min_us':>8s}"]
+    for name, n, avg, med, mn in sorted(rows):
+        lines.append(f"{name[:70]:70s} {n:5d} {avg:8.2f} {med:8.2f} {mn:8.2f}")
+    return "\n".join(lines)
+
+
+def read_counter(path: str, counter: str):
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic(fetch_csv: str, write_csv: str, copy_mib: int) -> dict:
+    fetch = read_counter(fetch_csv, "FETCH_SIZE")
+    write = read_counter(write_csv, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+
+    def copy_reading(d):
+        vals = [v for name, vs in d.items() if "copyBuffer" in name for v in vs]
+        # the calibration copy is the largest blit of the run
+        return max(vals)
+
+    f_scale = copy_kib / copy_reading(fetch)
+    w_scale = copy_kib / copy_reading(write)
+    res = {"source_sha256": hashlib.sha256(open(SRC, "rb").read()).hexdigest(),
+           "copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for kind in ("encode", "decode"):
+        fv = [v for n, vs in fetch.items() if kernel_kind(n) == kind for v in vs]
+        wv = [v for n, vs in write.items() if kernel_kind(n) == kind for v in vs]
+        if fv and wv:
+            res["kernels"][kind] = {
+                "fetch_kib_raw": statistics.median(fv), "write_kib_raw": statistics.median(wv),
+                "fetch_bytes": int(statistics.median(fv) * f_scale * 1024),
+                "write_bytes": int(statistics.median(wv) * w_scale * 1024),
+            }
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("csv")
+    c = sub.add_parser("traffic")
+    c.add_argument("fetch_csv")
+    c.add_argument("write_csv")
+    c.add_argument("--copy-mib", type=int, required=True)
+    c.add_argument("--json")
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        print(trace_summary(a.csv))
+    else:
+        res = traffic(a.fetch_csv, a.write_csv, a.copy_mib)
+        txt = json.dumps(res, indent=1)
+        if a.json:
+            with open(a.json, "w") as f:
+                f.write(txt + "\n")
+        print(txt)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

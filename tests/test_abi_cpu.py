@@ -86,10 +86,12 @@ def test_encode_argument_validation():
     assert _enc(k=FAKE + 8) == tq.TQ_E_ALIGN
     assert _enc(planes=[FAKE + 8, FAKE, FAKE, FAKE, FAKE]) == tq.TQ_E_ALIGN  # 4-bit codes need 16 B
     assert _enc(planes=[FAKE, FAKE + 1, FAKE, FAKE, FAKE]) == tq.TQ_E_ALIGN
-    # a side that is not encoded is not validated
-    assert _enc(v=None, cfg=(128, 4, 7, 0), planes=[FAKE, FAKE, FAKE, None, None]) != tq.TQ_E_BITS or True
-    # zero tokens is a no-op that launches nothing
+    # the value side's bits and planes are not checked when only keys are encoded
+    # (tokens=0 keeps the call from launching)
+    assert _enc(v=None, cfg=(128, 4, 7, 0), planes=[FAKE, FAKE, FAKE, None, None], tokens=0) == tq.TQ_OK
+    # zero tokens is a no-op that launches nothing and reads no pointer
     assert _enc(tokens=0) == tq.TQ_OK
+    assert _enc(k=None, v=None, tokens=0, planes=[None] * 5) == tq.TQ_OK
 
 
 def test_decode_argument_validation():
@@ -103,11 +105,13 @@ def test_decode_argument_validation():
     assert _dec(vout=FAKE + 4) == tq.TQ_E_ALIGN
     assert _dec(planes=[FAKE, FAKE, FAKE, None, FAKE]) == tq.TQ_E_NULL
     assert _dec(tokens=0) == tq.TQ_OK
+    assert _dec(kout=None, vout=None, tokens=0, planes=[None] * 5) == tq.TQ_OK
 
 
 def test_unrotate_argument_validation():
     L = tq.lib()
     assert L.tq_unrotate_values(None, FAKE, 0, 4, 128, None) == tq.TQ_E_NULL
+    assert L.tq_unrotate_values(None, None, 0, 0, 128, None) == tq.TQ_OK
     assert L.tq_unrotate_values(FAKE, FAKE, 0, 4, 100, None) == tq.TQ_E_HEAD_DIM
     assert L.tq_unrotate_values(FAKE, FAKE, 3, 4, 128, None) == tq.TQ_E_DTYPE
     assert L.tq_unrotate_values(FAKE, FAKE, 0, -1, 128, None) == tq.TQ_E_SHAPE

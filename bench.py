@@ -18,7 +18,6 @@ the host as a baseline. Diagnostics go to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -31,7 +30,6 @@ if ROOT not in sys.path:
 
 METRIC = "KV tokens/sec encode+decode (d=128, 4-bit) and achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-SRC = os.path.join(ROOT, "kv_cache_quantization_tq_amd", "csrc", "tq_codec.hip")
 TRAFFIC = os.path.join(ROOT, "profiles", "prefill_hbm_traffic.json")
 
 
@@ -50,8 +48,8 @@ def algorithmic_bytes(w):
 
 
 def source_digest():
-    with open(SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    from kv_cache_quantization_tq_amd.build import source_digest as digest
+    return digest()
 
 
 def measured_traffic(kernel: str):

@@ -2,20 +2,29 @@
 
     python -m kv_cache_quantization_tq_amd.build
 
-Always recompiles. Flags:
+Always recompiles. Each translation unit (the host API and one kernel unit
+per head_dim) compiles in its own hipcc process, in parallel, then one link
+step produces the shared library. Flags:
   -ffp-contract=off          products are rounded before they are added, as
                              the binary32 definition of every step requires;
   -packed-fp32-ops disabled  no v_pk_*_f32 instructions are generated.
+Extra -D flags (compile-time tuning knobs of tq_device.h) may be passed
+through the TQ_EXTRA_FLAGS environment variable.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import glob
+import hashlib
 import os
+import shlex
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "tq_codec.hip")
+CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
@@ -24,7 +33,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=off",
     "-fconstexpr-steps=50000000",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -33,32 +41,68 @@ HIPCC_FLAGS = [
 ]
 
 
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def source_digest() -> str:
+    """SHA-256 over every codec source and the public header."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "tq.h")]:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
-    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
-        if cand and (os.path.isabs(cand) and os.path.exists(cand) or not os.path.isabs(cand)):
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
             return cand
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp, SRC]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _flags():
+    return HIPCC_FLAGS + shlex.split(os.environ.get("TQ_EXTRA_FLAGS", "")) + \
+        ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed building {SRC}")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError("hipcc failed: " + " ".join(cmd[-3:]))
+    return r
 
 
-def build_asm(out: str) -> None:
-    """Device assembly of the codec (for reading the generated ISA)."""
-    cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], "--cuda-device-only", "-S",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), "-o", out, SRC]
-    subprocess.run(cmd, check=True)
+def build(verbose: bool = False, out: str = LIB) -> str:
+    with tempfile.TemporaryDirectory(prefix="tq_build_") as tmp:
+        objs, cmds = [], []
+        for src in sources():
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            objs.append(obj)
+            cmds.append([hipcc(), *_flags(), "-c", "-o", obj, src])
+        workers = min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
+        with cf.ThreadPoolExecutor(workers) as ex:
+            for cmd, _ in zip(cmds, ex.map(_run, cmds)):
+                if verbose:
+                    print(" ".join(cmd), flush=True)
+        tmp_lib = out + ".tmp"
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs]
+        if verbose:
+            print(" ".join(link), flush=True)
+        _run(link)
+        os.replace(tmp_lib, out)
+    return out
+
+
+def build_asm(out_dir: str) -> None:
+    """Device assembly of every kernel unit (for reading the generated ISA)."""
+    os.makedirs(out_dir, exist_ok=True)
+    cmds = [[hipcc(), *[f for f in _flags() if f != "-fPIC"], "--cuda-device-only", "-S",
+             "-o", os.path.join(out_dir, os.path.basename(s) + ".s"), s] for s in sources()]
+    with cf.ThreadPoolExecutor(8) as ex:
+        list(ex.map(_run, cmds))
 
 
 if __name__ == "__main__":

@@ -1,5 +1,7 @@
-// tq_codec.hip -- TurboQuant KV-cache codec for AMD MI355X (gfx950): kernels
-// and the C ABI declared in include/tq.h.
+// tq_device.h -- device code of the TurboQuant KV-cache codec for AMD MI355X
+// (gfx950): tables, transform, bin search, packing and the kernel templates.
+// Each kernel translation unit includes it and instantiates the kernels of one
+// head_dim; the host side (tq_api.hip) includes it for the shared tables.
 //
 // The codec is the one on the page "@mlx-bun/inference 0.0.0-stage -> 1.0.0",
 // package/src/kernels/turboquant/ops.ts (fwht, searchsorted, encodeKeys,
@@ -31,6 +33,8 @@
 // whose cells are narrower than the closest pair of boundaries, so one
 // final comparison against the single boundary a cell may hold gives the
 // exact count.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -38,23 +42,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#include <mutex>
-#include <unordered_map>
 
-#include "tq.h"
 #include "tq_tables.h"
 
 namespace {
 
 // Compile-time tuning knobs (defaults are the measured best on MI355X):
-//   TQ_ENCODE_PREFETCH_K  load the next tile's keys while encoding values;
-//   TQ_ENCODE_WAVES       if > 0, target this many wavefronts per SIMD
-//                         (caps the registers the encoder may use).
-#ifndef TQ_ENCODE_PREFETCH_K
-#define TQ_ENCODE_PREFETCH_K 1
-#endif
+//   TQ_ENCODE_WAVES, TQ_DECODE_WAVES  if > 0, target this many wavefronts
+//                         per SIMD (caps the registers the kernel may use).
 #ifndef TQ_ENCODE_WAVES
 #define TQ_ENCODE_WAVES 0
+#endif
+#ifndef TQ_DECODE_WAVES
+#define TQ_DECODE_WAVES 0
 #endif
 
 constexpr int kGroup = 32;
@@ -500,6 +500,76 @@ __device__ __forceinline__ float quot(float a, float b, float r)
     return __builtin_fmaf(e, r, q0);
 }
 
+// x / se - zp for element j (IEEE division on the slow path)
+__device__ __forceinline__ float key_shifted(float x, float se, float r, float zp, bool ieee)
+{
+    return (ieee ? x / se : quot(x, se, r)) - zp;
+}
+
+// Codes of one key group, packed (element j at bits [j*KB, j*KB+KB)).
+// Unsigned codes: clip(rint(d), 0, maxv) = rint(clip(d, 0, maxv)) for the
+// integer bounds, and v_cvt_pk_u8_f32 rounds to nearest even, saturates to
+// [0, 255] and inserts the byte in one instruction; for 2-, 4- and 8-bit
+// codes the bytes are laid out so that shifting whole dwords interleaves
+// them into the bit stream (4-bit: even elements in one dword, odd ones in
+// another shifted by 4; 2-bit: four dwords shifted by 0, 2, 4, 6). Signed
+// 8-bit codes round, clip to [-127, 127] and take the low byte of each.
+template <int KB, bool KS>
+__device__ __forceinline__ void key_codes(const float (&x)[kGroup], float se, float r, float zp, uint32_t (&w)[KB],
+                                          bool ieee)
+{
+    constexpr float maxv = KS ? 127.0f : (float)((1 << KB) - 1);
+    if constexpr (KS) {
+        uint32_t q[kGroup];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+            q[j] = (uint32_t)(int32_t)__builtin_amdgcn_fmed3f(rintf(key_shifted(x[j], se, r, zp, ieee)), -maxv, maxv);
+        pack32<KB>(q, w);
+    } else if constexpr (KB == 8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) b = __builtin_amdgcn_cvt_pk_u8_f32(key_shifted(x[4 * k + t], se, r, zp, ieee), t, b);
+            w[k] = b;
+        }
+    } else if constexpr (KB == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t ev = 0, od = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float de = __builtin_amdgcn_fmed3f(key_shifted(x[8 * k + 2 * t], se, r, zp, ieee), 0.0f, maxv);
+                const float dd = __builtin_amdgcn_fmed3f(key_shifted(x[8 * k + 2 * t + 1], se, r, zp, ieee), 0.0f, maxv);
+                ev = __builtin_amdgcn_cvt_pk_u8_f32(de, t, ev);
+                od = __builtin_amdgcn_cvt_pk_u8_f32(dd, t, od);
+            }
+            w[k] = ev | (od << 4);
+        }
+    } else if constexpr (KB == 2) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t d4[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float d = __builtin_amdgcn_fmed3f(key_shifted(x[16 * k + 4 * t + rr], se, r, zp, ieee), 0.0f, maxv);
+                    d4[rr] = __builtin_amdgcn_cvt_pk_u8_f32(d, t, d4[rr]);
+                }
+            }
+            w[k] = d4[0] | (d4[1] << 2) | (d4[2] << 4) | (d4[3] << 6);
+        }
+    } else {
+        uint32_t q[kGroup];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+            q[j] = __builtin_amdgcn_cvt_pk_u8_f32(
+                __builtin_amdgcn_fmed3f(key_shifted(x[j], se, r, zp, ieee), 0.0f, maxv), 0, 0u);
+        pack32<KB>(q, w);
+    }
+}
+
 template <int KB, bool KS>
 __device__ __forceinline__ void key_encode_group(const float (&x)[kGroup], uint8_t *codes,
                                                  uint16_t *scale_out, uint16_t *zero_out)
@@ -521,26 +591,12 @@ __device__ __forceinline__ void key_encode_group(const float (&x)[kGroup], uint8
     const float r = 1.0f / se;
     const float amax = fmaxf(fabsf(mn), fabsf(mx));
     const bool fast = (se < 1e30f) && (amax * r < 1e30f);
-    const float lo = KS ? -(float)maxv : 0.0f;
-    const float hi = (float)maxv;
-    uint32_t q[kGroup];
-    if (fast) {
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-            const float o = quot(x[j], se, r);
-            const float c = __builtin_amdgcn_fmed3f(rintf(o - zp), lo, hi);
-            q[j] = (uint32_t)(int32_t)c;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-            const float o = x[j] / se;
-            const float c = __builtin_amdgcn_fmed3f(rintf(o - zp), lo, hi);
-            q[j] = (uint32_t)(int32_t)c;
-        }
-    }
     uint32_t w[KB];
-    pack32<KB>(q, w);
+    if (fast) {
+        key_codes<KB, KS>(x, se, r, zp, w, /*ieee=*/false);
+    } else {
+        key_codes<KB, KS>(x, se, r, zp, w, /*ieee=*/true);
+    }
     store_codes<KB>(codes, w);
     *scale_out = f32_to_f16_bits(scale);
     *zero_out = f32_to_f16_bits(zp);
@@ -614,12 +670,21 @@ __device__ __forceinline__ void store_tile(void *base, int64_t row0, int64_t row
     uint8_t *tile = reinterpret_cast<uint8_t *>(base) + row0 * (int64_t)(D * elem_bytes);
     const int c_lo = lane % S::LPI;
     const int sub = lane / S::LPI;
+    uint4 v[S::CH];
 #pragma unroll
-    for (int i = 0; i < S::CH; ++i) {
-        const int c = S::LPI * i + c_lo;               // piece = writer lane
-        const uint4 v = stage[c * S::STRIDE + sub];
-        if (row0 + c / G < rows)
-            *reinterpret_cast<uint4 *>(tile + (c * S::CH + sub) * 16) = v;
+    for (int i = 0; i < S::CH; ++i) v[i] = stage[(S::LPI * i + c_lo) * S::STRIDE + sub];
+    if (row0 + kWave / G <= rows) {
+        // whole tile in range (wave-uniform branch)
+#pragma unroll
+        for (int i = 0; i < S::CH; ++i)
+            *reinterpret_cast<uint4 *>(tile + (uint32_t)(((S::LPI * i + c_lo) * S::CH + sub) * 16)) = v[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < S::CH; ++i) {
+            const int c = S::LPI * i + c_lo; // piece = writer lane
+            if (row0 + c / G < rows)
+                *reinterpret_cast<uint4 *>(tile + (uint32_t)((c * S::CH + sub) * 16)) = v[i];
+        }
     }
 }
 
@@ -671,9 +736,10 @@ __device__ __forceinline__ void raw_to_f32(const RawGroup<BF16> &r, uint32_t sma
     }
 }
 
-// Tile loop of the encoder for one key mode (KB = 0: values only). A
-// wavefront walks tiles t, t + stride, ...; the key input of the next tile
-// is loaded while the current tile's values are processed.
+// Tile loop of the encoder for one key mode (KB = 0: values only): a
+// wavefront walks tiles t, t + stride, ... Loads always read a valid row
+// (rows past the end read the last row, whose results are not stored), so
+// they need no branch.
 template <int D, int VB, int KB, bool KS, bool BF16IN>
 __device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const void *__restrict__ vin, int64_t rows,
                                             uint8_t *__restrict__ kc, uint16_t *__restrict__ ks,
@@ -684,7 +750,7 @@ __device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const 
     constexpr int RPW = kWave / G;
     constexpr bool HASK = KB != 0;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); // wavefront-uniform
     const int g = lane % G;
     const int rl = lane / G;
     const uint32_t smask = dev_sign<D>(g);
@@ -692,41 +758,22 @@ __device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const 
     const bool hasv = vin != nullptr;
     const int64_t tiles = (rows + RPW - 1) / RPW;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-    int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    constexpr bool PREFETCH = HASK && TQ_ENCODE_PREFETCH_K;
-    RawGroup<BF16IN> kraw;
-    if constexpr (PREFETCH) {
-        const int64_t row = t * RPW + rl;
-        if (t < tiles && row < rows) load_raw<BF16IN>(kin, row * D + (int64_t)g * kGroup, kraw);
-    }
-    for (; t < tiles; t += stride) {
+    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave; t < tiles; t += stride) {
         const int64_t row = t * RPW + rl;
         const bool act = row < rows;
-        const int64_t e0 = row * D + (int64_t)g * kGroup;
         const int64_t grp = row * G + g;
-        RawGroup<BF16IN> vraw;
-        if (hasv && act) load_raw<BF16IN>(vin, e0, vraw);
+        const int64_t e0 = (act ? row : rows - 1) * D + (int64_t)g * kGroup;
+        RawGroup<BF16IN> kraw, vraw;
+        if constexpr (HASK) load_raw<BF16IN>(kin, e0, kraw);
+        if (hasv) load_raw<BF16IN>(vin, e0, vraw);
         if constexpr (HASK) {
-            if (act) {
-                if constexpr (!PREFETCH) load_raw<BF16IN>(kin, e0, kraw);
-                float x[kGroup];
-                raw_to_f32<BF16IN>(kraw, 0u, x);
-                key_encode_group<KB, KS>(x, kc + grp * (4 * KB), ks + grp, kz + grp);
-            }
-            if constexpr (PREFETCH) {
-                const int64_t tn = t + stride;
-                const int64_t rown = tn * RPW + rl;
-                if (tn < tiles && rown < rows) load_raw<BF16IN>(kin, rown * D + (int64_t)g * kGroup, kraw);
-            }
+            float x[kGroup];
+            raw_to_f32<BF16IN>(kraw, 0u, x);
+            if (act) key_encode_group<KB, KS>(x, kc + grp * (4 * KB), ks + grp, kz + grp);
         }
         if (hasv) {
             float y[kGroup];
-            if (act) {
-                raw_to_f32<BF16IN>(vraw, smask, y);
-            } else {
-#pragma unroll
-                for (int j = 0; j < kGroup; ++j) y[j] = 0.0f;
-            }
+            raw_to_f32<BF16IN>(vraw, smask, y);
             hadamard<D>(y, rot);
             float ss = 0.0f;
 #pragma unroll
@@ -799,28 +846,29 @@ __device__ __forceinline__ void load_group_codes(const uint8_t *__restrict__ kc,
                                                  const uint16_t *__restrict__ vs, int64_t row, int64_t rows, int g,
                                                  bool hasv, GroupCodes<KB, VB> &c)
 {
+    // always a valid row (rows past the end read the last row, whose
+    // results are not stored): branch-free loads keep wait counts exact
     constexpr int G = D / kGroup;
-    const int64_t grp = row * G + g;
+    const int64_t grp = (row < rows ? row : rows - 1) * G + g;
+    if constexpr (KB != 0) {
+        load_codes<KB>(kc + grp * (4 * KB), c.kw);
+        c.ks = ks[grp];
+        c.kz = kz[grp];
+    } else {
+        c.kw[0] = 0;
+        c.ks = c.kz = 0;
+    }
+    if (hasv) {
+        load_codes<VB>(vc + grp * (4 * VB), c.vw);
+        c.vs = vs[grp];
+    } else {
 #pragma unroll
-    for (int k = 0; k < (KB > 0 ? KB : 1); ++k) c.kw[k] = 0;
-#pragma unroll
-    for (int k = 0; k < VB; ++k) c.vw[k] = 0;
-    c.ks = c.kz = c.vs = 0;
-    if (row < rows) {
-        if constexpr (KB != 0) {
-            load_codes<KB>(kc + grp * (4 * KB), c.kw);
-            c.ks = ks[grp];
-            c.kz = kz[grp];
-        }
-        if (hasv) {
-            load_codes<VB>(vc + grp * (4 * VB), c.vw);
-            c.vs = vs[grp];
-        }
+        for (int k = 0; k < VB; ++k) c.vw[k] = 0;
+        c.vs = 0;
     }
 }
 
-// Tile loop of the decoder for one key mode (KB = 0: values only). The
-// codes of the next tile are loaded before the current tile is decoded.
+// Tile loop of the decoder for one key mode (KB = 0: values only).
 template <int D, int VB, int KB, bool KS, bool BF16OUT>
 __device__ __forceinline__ void decode_loop(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks,
                                             const uint16_t *__restrict__ kz, const uint8_t *__restrict__ vc,
@@ -832,7 +880,7 @@ __device__ __forceinline__ void decode_loop(const uint8_t *__restrict__ kc, cons
     constexpr int RPW = kWave / G;
     constexpr bool HASK = KB != 0;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); // wavefront-uniform
     const int g = lane % G;
     const int rl = lane / G;
     const uint32_t smask = rotated ? 0u : dev_sign<D>(g);
@@ -840,14 +888,9 @@ __device__ __forceinline__ void decode_loop(const uint8_t *__restrict__ kc, cons
     const bool hasv = vout != nullptr;
     const int64_t tiles = (rows + RPW - 1) / RPW;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-
-    int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    GroupCodes<KB, VB> cur;
-    load_group_codes<D, VB, KB>(kc, ks, kz, vc, vs, t < tiles ? t * RPW + rl : rows, rows, g, hasv, cur);
-    for (; t < tiles; t += stride) {
-        const int64_t tn = t + stride;
-        GroupCodes<KB, VB> nxt;
-        load_group_codes<D, VB, KB>(kc, ks, kz, vc, vs, tn < tiles ? tn * RPW + rl : rows, rows, g, hasv, nxt);
+    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave; t < tiles; t += stride) {
+        GroupCodes<KB, VB> cur;
+        load_group_codes<D, VB, KB>(kc, ks, kz, vc, vs, t * RPW + rl, rows, g, hasv, cur);
         const int64_t row0 = t * RPW;
         if constexpr (HASK) {
             float y[kGroup];
@@ -870,18 +913,17 @@ __device__ __forceinline__ void decode_loop(const uint8_t *__restrict__ kc, cons
             if (!rotated) hadamard<D>(y, rot);
             store_tile<D, BF16OUT>(vout, row0, rows, smask, y, stage);
         }
-#pragma unroll
-        for (int k = 0; k < (KB > 0 ? KB : 1); ++k) cur.kw[k] = nxt.kw[k];
-#pragma unroll
-        for (int k = 0; k < VB; ++k) cur.vw[k] = nxt.vw[k];
-        cur.ks = nxt.ks;
-        cur.kz = nxt.kz;
-        cur.vs = nxt.vs;
     }
 }
 
+#if TQ_DECODE_WAVES > 0
+#define TQ_DECODE_ATTR __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(TQ_DECODE_WAVES)))
+#else
+#define TQ_DECODE_ATTR __launch_bounds__(kBlockThreads)
+#endif
+
 template <int D, int VB, bool BF16OUT>
-__global__ void __launch_bounds__(kBlockThreads)
+__global__ void TQ_DECODE_ATTR
 decode_kernel(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks, const uint16_t *__restrict__ kz,
               const uint8_t *__restrict__ vc, const uint16_t *__restrict__ vs, int64_t rows, int32_t kmode,
               int32_t rotated, void *__restrict__ kout, void *__restrict__ vout)
@@ -895,7 +937,7 @@ decode_kernel(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks, c
         for (int i = threadIdx.x; i < NC; i += kBlockThreads) cent[i] = src[i];
         __syncthreads();
     }
-    uint4 *stage = stage_all + (threadIdx.x / kWave) * S::WORDS;
+    uint4 *stage = stage_all + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * S::WORDS;
     switch (kmode) {
     case 2: decode_loop<D, VB, 2, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
     case 3: decode_loop<D, VB, 3, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
@@ -918,7 +960,7 @@ unrotate_kernel(const void *x, void *out, int64_t rows)
     using S = Stage<BF16>;
     __shared__ uint4 stage_all[kWavesPerBlock * S::WORDS];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); // wavefront-uniform
     uint4 *stage = stage_all + wave * S::WORDS;
     const int g = lane % G;
     const int rl = lane / G;
@@ -929,320 +971,14 @@ unrotate_kernel(const void *x, void *out, int64_t rows)
          t += (int64_t)gridDim.x * kWavesPerBlock) {
         const int64_t row0 = t * RPW;
         const int64_t row = row0 + rl;
-        const bool act = row < rows;
-        const int64_t e0 = row * D + (int64_t)g * kGroup;
+        const int64_t e0 = (row < rows ? row : rows - 1) * D + (int64_t)g * kGroup;
         float y[kGroup];
-        if (act) {
-            RawGroup<BF16> raw;
-            load_raw<BF16>(x, e0, raw);
-            raw_to_f32<BF16>(raw, 0u, y);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kGroup; ++j) y[j] = 0.0f;
-        }
+        RawGroup<BF16> raw;
+        load_raw<BF16>(x, e0, raw);
+        raw_to_f32<BF16>(raw, 0u, y);
         hadamard<D>(y, rot);
         store_tile<D, BF16>(out, row0, rows, smask, y, stage);
     }
 }
 
-// ---------------------------------------------------------------------------
-// Host side
-// ---------------------------------------------------------------------------
-
-bool valid_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
-bool valid_bits(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 8; }
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-uintptr_t code_align(int32_t bits) { return (bits == 4 || bits == 8) ? 16 : 8; }
-
-// Persistent grid: as many blocks as can be resident at once (occupancy of
-// the kernel times the device's compute units), capped by the number of
-// tiles. TQ_BLOCKS_PER_CU, if set, replaces the occupancy figure (for
-// tuning sweeps).
-int64_t grid_for(const void *fn, int64_t rows, int32_t d)
-{
-    static std::mutex mu;
-    static std::unordered_map<const void *, int> occupancy;
-    static int cus[64] = {0};
-    static int env_per_cu = -1;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    int per_cu = 0, ncu = 0;
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        if (env_per_cu < 0) {
-            const char *e = getenv("TQ_BLOCKS_PER_CU");
-            env_per_cu = (e != nullptr && atoi(e) > 0) ? atoi(e) : 0;
-        }
-        if (cus[dev] == 0) {
-            int n = 0;
-            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-            cus[dev] = n;
-        }
-        ncu = cus[dev];
-        auto it = occupancy.find(fn);
-        if (it == occupancy.end()) {
-            int b = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, kBlockThreads, 0) != hipSuccess || b <= 0) b = 2;
-            it = occupancy.emplace(fn, b).first;
-        }
-        per_cu = env_per_cu > 0 ? env_per_cu : it->second;
-    }
-    const int64_t rpw = kWave / (d / kGroup);
-    const int64_t tiles = (rows + rpw - 1) / rpw;
-    int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t resident = (int64_t)per_cu * ncu;
-    if (blocks > resident) blocks = resident;
-    return blocks < 1 ? 1 : blocks;
-}
-
-int32_t check_rows(int64_t tokens, int32_t heads, int64_t *rows)
-{
-    if (tokens < 0 || heads < 1) return TQ_E_SHAPE;
-    if (tokens > (int64_t)1 << 40 || heads > (1 << 20)) return TQ_E_SHAPE;
-    *rows = tokens * heads;
-    return TQ_OK;
-}
-
-int32_t key_mode(const tq_config *cfg) { return cfg->k_bits | (cfg->k_signed ? 16 : 0); }
-
-typedef void (*EncodeFn)(const void *, const void *, int64_t, int32_t, uint8_t *, uint16_t *, uint16_t *,
-                         uint8_t *, uint16_t *);
-typedef void (*DecodeFn)(const uint8_t *, const uint16_t *, const uint16_t *, const uint8_t *,
-                         const uint16_t *, int64_t, int32_t, int32_t, void *, void *);
-typedef void (*UnrotateFn)(const void *, void *, int64_t);
-
-template <int D, bool BF> EncodeFn pick_encode_vb(int32_t vb)
-{
-    switch (vb) {
-    case 2: return encode_kernel<D, 2, BF>;
-    case 3: return encode_kernel<D, 3, BF>;
-    case 4: return encode_kernel<D, 4, BF>;
-    case 5: return encode_kernel<D, 5, BF>;
-    case 8: return encode_kernel<D, 8, BF>;
-    default: return nullptr;
-    }
-}
-
-template <bool BF> EncodeFn pick_encode(int32_t d, int32_t vb)
-{
-    switch (d) {
-    case 64: return pick_encode_vb<64, BF>(vb);
-    case 128: return pick_encode_vb<128, BF>(vb);
-    case 256: return pick_encode_vb<256, BF>(vb);
-    case 512: return pick_encode_vb<512, BF>(vb);
-    default: return nullptr;
-    }
-}
-
-template <int D, bool BF> DecodeFn pick_decode_vb(int32_t vb)
-{
-    switch (vb) {
-    case 2: return decode_kernel<D, 2, BF>;
-    case 3: return decode_kernel<D, 3, BF>;
-    case 4: return decode_kernel<D, 4, BF>;
-    case 5: return decode_kernel<D, 5, BF>;
-    case 8: return decode_kernel<D, 8, BF>;
-    default: return nullptr;
-    }
-}
-
-template <bool BF> DecodeFn pick_decode(int32_t d, int32_t vb)
-{
-    switch (d) {
-    case 64: return pick_decode_vb<64, BF>(vb);
-    case 128: return pick_decode_vb<128, BF>(vb);
-    case 256: return pick_decode_vb<256, BF>(vb);
-    case 512: return pick_decode_vb<512, BF>(vb);
-    default: return nullptr;
-    }
-}
-
-template <bool BF> UnrotateFn pick_unrotate(int32_t d)
-{
-    switch (d) {
-    case 64: return unrotate_kernel<64, BF>;
-    case 128: return unrotate_kernel<128, BF>;
-    case 256: return unrotate_kernel<256, BF>;
-    case 512: return unrotate_kernel<512, BF>;
-    default: return nullptr;
-    }
-}
-
-int32_t launch_status()
-{
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
-}
-
-
 } // namespace
-
-// ---------------------------------------------------------------------------
-// C ABI
-// ---------------------------------------------------------------------------
-
-extern "C" {
-
-int64_t tq_packed_dim(int32_t dim, int32_t bits)
-{
-    if (dim < 1 || bits < 1 || bits > 8) return -TQ_E_BITS;
-    if (((int64_t)dim * bits) % 8 != 0) return -TQ_E_ALIGN;
-    return ((int64_t)dim * bits) / 8;
-}
-
-const char *tq_status_string(int32_t status)
-{
-    switch (status) {
-    case TQ_OK: return "ok";
-    case TQ_E_NULL: return "a required pointer is NULL";
-    case TQ_E_HEAD_DIM: return "head_dim must be 64, 128, 256 or 512";
-    case TQ_E_BITS: return "bits must be 2, 3, 4, 5 or 8 (signed keys: 8 only)";
-    case TQ_E_ALIGN: return "misaligned pointer or dim*bits not a whole number of bytes";
-    case TQ_E_DTYPE: return "dtype must be TQ_F32 or TQ_BF16";
-    case TQ_E_SHAPE: return "tokens must be >= 0 and heads >= 1 (row count within range)";
-    case TQ_E_HIP: return "HIP runtime error at kernel launch";
-    default: return "unknown status";
-    }
-}
-
-int32_t tq_encode_kv(const void *k, const void *v, int32_t in_dtype, int64_t tokens, int32_t heads,
-                     const tq_config *cfg, const tq_packed_kv *out, void *stream)
-{
-    if (cfg == nullptr || out == nullptr) return TQ_E_NULL;
-    if (!valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
-    if (in_dtype != TQ_F32 && in_dtype != TQ_BF16) return TQ_E_DTYPE;
-    int64_t rows = 0;
-    const int32_t st = check_rows(tokens, heads, &rows);
-    if (st != TQ_OK) return st;
-    if (rows == 0) return TQ_OK;
-    if (k == nullptr && v == nullptr) return TQ_E_NULL;
-    if (k != nullptr) {
-        if (!valid_bits(cfg->k_bits) || (cfg->k_signed != 0 && cfg->k_bits != 8) ||
-            (cfg->k_signed != 0 && cfg->k_signed != 1))
-            return TQ_E_BITS;
-        if (out->k_codes == nullptr || out->k_scale == nullptr || out->k_zero == nullptr) return TQ_E_NULL;
-        if (!aligned(k, 16) || !aligned(out->k_codes, code_align(cfg->k_bits)) || !aligned(out->k_scale, 2) ||
-            !aligned(out->k_zero, 2))
-            return TQ_E_ALIGN;
-    }
-    if (v != nullptr) {
-        if (!valid_bits(cfg->v_bits)) return TQ_E_BITS;
-        if (out->v_codes == nullptr || out->v_scale == nullptr) return TQ_E_NULL;
-        if (!aligned(v, 16) || !aligned(out->v_codes, code_align(cfg->v_bits)) || !aligned(out->v_scale, 2))
-            return TQ_E_ALIGN;
-    }
-    const int32_t vb = (v != nullptr) ? cfg->v_bits : 4;
-    EncodeFn fn = (in_dtype == TQ_BF16) ? pick_encode<true>(cfg->head_dim, vb) : pick_encode<false>(cfg->head_dim, vb);
-    const int32_t kmode = (k != nullptr) ? key_mode(cfg) : KMODE_NONE;
-    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for((const void *)fn, rows, cfg->head_dim)), dim3(kBlockThreads), 0,
-                       (hipStream_t)stream, k, v, rows, kmode, (uint8_t *)out->k_codes, (uint16_t *)out->k_scale,
-                       (uint16_t *)out->k_zero, (uint8_t *)out->v_codes, (uint16_t *)out->v_scale);
-    return launch_status();
-}
-
-int32_t tq_decode_kv(const tq_packed_kv *in, int64_t tokens, int32_t heads, const tq_config *cfg, void *k_out,
-                     void *v_out, int32_t out_dtype, int32_t flags, void *stream)
-{
-    if (cfg == nullptr || in == nullptr) return TQ_E_NULL;
-    if (!valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
-    if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_E_DTYPE;
-    if ((flags & ~TQ_DECODE_ROTATED_V) != 0) return TQ_E_SHAPE;
-    int64_t rows = 0;
-    const int32_t st = check_rows(tokens, heads, &rows);
-    if (st != TQ_OK) return st;
-    if (rows == 0) return TQ_OK;
-    if (k_out == nullptr && v_out == nullptr) return TQ_E_NULL;
-    if (k_out != nullptr) {
-        if (!valid_bits(cfg->k_bits) || (cfg->k_signed != 0 && cfg->k_bits != 8) ||
-            (cfg->k_signed != 0 && cfg->k_signed != 1))
-            return TQ_E_BITS;
-        if (in->k_codes == nullptr || in->k_scale == nullptr || in->k_zero == nullptr) return TQ_E_NULL;
-        if (!aligned(k_out, 16) || !aligned(in->k_codes, code_align(cfg->k_bits)) || !aligned(in->k_scale, 2) ||
-            !aligned(in->k_zero, 2))
-            return TQ_E_ALIGN;
-    }
-    if (v_out != nullptr) {
-        if (!valid_bits(cfg->v_bits)) return TQ_E_BITS;
-        if (in->v_codes == nullptr || in->v_scale == nullptr) return TQ_E_NULL;
-        if (!aligned(v_out, 16) || !aligned(in->v_codes, code_align(cfg->v_bits)) || !aligned(in->v_scale, 2))
-            return TQ_E_ALIGN;
-    }
-    const int32_t vb = (v_out != nullptr) ? cfg->v_bits : 4;
-    DecodeFn fn = (out_dtype == TQ_BF16) ? pick_decode<true>(cfg->head_dim, vb) : pick_decode<false>(cfg->head_dim, vb);
-    const int32_t kmode = (k_out != nullptr) ? key_mode(cfg) : KMODE_NONE;
-    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for((const void *)fn, rows, cfg->head_dim)), dim3(kBlockThreads), 0,
-                       (hipStream_t)stream, (const uint8_t *)in->k_codes, (const uint16_t *)in->k_scale,
-                       (const uint16_t *)in->k_zero, (const uint8_t *)in->v_codes, (const uint16_t *)in->v_scale,
-                       rows, kmode, (int32_t)((flags & TQ_DECODE_ROTATED_V) != 0), k_out, v_out);
-    return launch_status();
-}
-
-int32_t tq_unrotate_values(const void *x, void *out, int32_t dtype, int64_t rows, int32_t head_dim, void *stream)
-{
-    if (!valid_head_dim(head_dim)) return TQ_E_HEAD_DIM;
-    if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_E_DTYPE;
-    if (rows < 0 || rows > ((int64_t)1 << 44)) return TQ_E_SHAPE;
-    if (rows == 0) return TQ_OK;
-    if (x == nullptr || out == nullptr) return TQ_E_NULL;
-    if (!aligned(x, 16) || !aligned(out, 16)) return TQ_E_ALIGN;
-    UnrotateFn fn = (dtype == TQ_BF16) ? pick_unrotate<true>(head_dim) : pick_unrotate<false>(head_dim);
-    hipLaunchKernelGGL(fn, dim3((uint32_t)grid_for((const void *)fn, rows, head_dim)), dim3(kBlockThreads), 0,
-                       (hipStream_t)stream, x, out, rows);
-    return launch_status();
-}
-
-int32_t tq_lloyd_max_table(int32_t bits, float *centroids, float *boundaries)
-{
-    if (!valid_bits(bits)) return TQ_E_BITS;
-    const float *c = nullptr, *b = nullptr;
-    switch (bits) {
-    case 2: c = LM<2>::c; b = LM<2>::b; break;
-    case 3: c = LM<3>::c; b = LM<3>::b; break;
-    case 4: c = LM<4>::c; b = LM<4>::b; break;
-    case 5: c = LM<5>::c; b = LM<5>::b; break;
-    default: c = LM<8>::c; b = LM<8>::b; break;
-    }
-    const int n = 1 << bits;
-    if (centroids != nullptr)
-        for (int i = 0; i < n; ++i) centroids[i] = c[i];
-    if (boundaries != nullptr)
-        for (int i = 0; i < n - 1; ++i) boundaries[i] = b[i];
-    return TQ_OK;
-}
-
-int32_t tq_sign_vector(int32_t head_dim, float *signs)
-{
-    if (!valid_head_dim(head_dim)) return TQ_E_HEAD_DIM;
-    if (signs == nullptr) return TQ_E_NULL;
-    const uint32_t *m = head_dim == 64 ? kSignMask64 : head_dim == 128 ? kSignMask128
-                      : head_dim == 256 ? kSignMask256 : kSignMask512;
-    for (int i = 0; i < head_dim; ++i) signs[i] = ((m[i / 32] >> (i % 32)) & 1u) ? -1.0f : 1.0f;
-    return TQ_OK;
-}
-
-int32_t tq_value_bin_host(int32_t bits, const float *z, int64_t n, uint8_t *idx)
-{
-    if (!valid_bits(bits)) return TQ_E_BITS;
-    if (n < 0) return TQ_E_SHAPE;
-    if (n > 0 && (z == nullptr || idx == nullptr)) return TQ_E_NULL;
-    static constexpr BinLut<2> l2{};
-    static constexpr BinLut<3> l3{};
-    static constexpr BinLut<4> l4{};
-    static constexpr BinLut<5> l5{};
-    static constexpr BinLut<8> l8{};
-    for (int64_t i = 0; i < n; ++i) {
-        // the kernels' fast path for |z| <= 6, the general path otherwise
-        const bool bounded = fabsf(z[i]) <= 6.0f;
-        uint32_t r = 0;
-        switch (bits) {
-        case 2: r = bounded ? bin_index_bounded<2>(z[i], l2.cell) : bin_index_any<2>(z[i], l2.cell); break;
-        case 3: r = bounded ? bin_index_bounded<3>(z[i], l3.cell) : bin_index_any<3>(z[i], l3.cell); break;
-        case 4: r = bounded ? bin_index_bounded<4>(z[i], l4.cell) : bin_index_any<4>(z[i], l4.cell); break;
-        case 5: r = bounded ? bin_index_bounded<5>(z[i], l5.cell) : bin_index_any<5>(z[i], l5.cell); break;
-        default: r = bounded ? bin_index_bounded<8>(z[i], l8.cell) : bin_index_any<8>(z[i], l8.cell); break;
-        }
-        idx[i] = (uint8_t)r;
-    }
-    return TQ_OK;
-}
-
-} // extern "C"

@@ -15,7 +15,6 @@ from __future__ import annotations
 
 import argparse
 import csv
-import hashlib
 import json
 import os
 import re
@@ -23,7 +22,6 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "csrc", "tq_codec.hip")
 
 
 def kernel_kind(name: str) -> str:
@@ -86,7 +84,8 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int) -> dict:
 
     f_scale = copy_kib / copy_reading(fetch)
     w_scale = copy_kib / copy_reading(write)
-    res = {"source_sha256": hashlib.sha256(open(SRC, "rb").read()).hexdigest(),
+    from kv_cache_quantization_tq_amd.build import source_digest
+    res = {"source_sha256": source_digest(),
            "copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     for kind in ("encode", "decode"):
         fv = [v for n, vs in fetch.items() if kernel_kind(n) == kind for v in vs]

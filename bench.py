@@ -1,23 +1,34 @@
 #!/usr/bin/env python3
 """Throughput of the TurboQuant KV-cache codec on one MI355X.
 
-A step is one pass of the whole hot path over the prefill workload (batch 1,
-8 KV heads, head_dim 128, 32768 tokens, bf16 K/V with per-channel scales;
-values 4-bit Lloyd-Max, keys 4-bit affine): encode K and V of every token
-into the packed planes, then decode every token back to bf16 K and V. The
-inputs are resident in HBM before timing starts. Steps rotate over several
-independent buffer sets so that the working set exceeds the 256 MB
-last-level cache and every step streams from HBM.
+    python bench.py [--workload prefill|small_head|long_decode|joint_large]
+                    [--steps K] [--warmup W]
 
-Prints one JSON line: value = KV tokens per second for encode + decode
-(one KV token = one position with K and V of all its heads), plus the
-roofline of the dominant kernel (algorithmic bytes / average kernel
-duration from HIP events on the launch stream) and the CPU oracle timed on
-the host as a baseline. Diagnostics go to stderr.
+The default workload is the headline one, prefill: batch 1, 8 KV heads,
+head_dim 128, 32768 tokens, bf16 K/V with per-channel scales; values 4-bit
+Lloyd-Max, keys 4-bit affine. What one step is:
+
+* prefill, small_head  encode K and V of every token into the packed planes,
+                       then decode every token back to bf16 K and V; steps
+                       rotate over enough independent buffer sets that a
+                       step's data cannot stay in the 256 MB last-level cache;
+* long_decode          append one token per head to a 131072-token cache
+                       (encode 8 rows at the cache's end), then decode the
+                       whole cache to bf16;
+* joint_large          one joint decode of packed K and V (262144 tokens x 8
+                       heads, head_dim 512) to bf16.
+
+Inputs are resident in HBM before timing starts. Prints one JSON line:
+value = KV tokens per second (one KV token = one position with K and V of
+all its heads; for the decode workloads, tokens decoded), the roofline of
+the dominant kernel (algorithmic bytes per launch / its average duration
+from HIP events recorded on the launch stream inside the timed loop), and
+the CPU oracle timed on the host as a baseline. Diagnostics go to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import json
 import math
 import os
@@ -28,38 +39,58 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-METRIC = "KV tokens/sec encode+decode (d=128, 4-bit) and achieved HBM GB/s vs peak"
+HEADLINE_METRIC = "KV tokens/sec encode+decode (d=128, 4-bit) and achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-TRAFFIC = os.path.join(ROOT, "profiles", "prefill_hbm_traffic.json")
+
+DESCRIPTION = {
+    "prefill": "prefill: batch 1, 8 KV heads, head_dim 128, 32768 tokens, bf16 K/V (N(0,1) x per-channel "
+               "log-uniform [0.1,10] scales); values 4-bit Lloyd-Max, keys 4-bit affine; encode all + decode "
+               "all to bf16",
+    "small_head": "small_head: batch 16 x 4096 tokens, 4 KV heads, head_dim 64, bf16 K/V Student-t(4) with 2 "
+                  "outlier channels per head x20; values 2-bit, keys 8-bit signed affine; encode all + decode "
+                  "all to bf16",
+    "long_decode": "long_decode: batch 1, 8 KV heads, head_dim 256, 131072 cached tokens (fp32 N(0,1)) at "
+                   "5-bit values / 4-bit keys; per step append 1 token per head, then decode the whole "
+                   "cache to bf16",
+    "joint_large": "joint_large: batch 4 x 65536 tokens, 8 KV heads, head_dim 512, bf16 N(0,1) with 1% of "
+                   "rows zeroed; values 8-bit (unpacked bytes), keys 4-bit; one joint K/V decode to bf16",
+}
+
+METRIC = {
+    "prefill": HEADLINE_METRIC,
+    "small_head": "KV tokens/sec encode+decode (d=64, V2/K8s) and achieved HBM GB/s vs peak",
+    "long_decode": "KV tokens/sec decoded per step (append 1 token + full decode, d=256, V5/K4) and "
+                   "achieved HBM GB/s vs peak",
+    "joint_large": "KV tokens/sec joint K/V decode (d=512, V8/K4) and achieved HBM GB/s vs peak",
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w):
-    """Bytes the method itself must move per launch (tables excluded)."""
-    d, R, G = w.head_dim, w.rows, w.head_dim // 32
+def row_bytes(w):
+    """Algorithmic bytes per row (one token of one head) moved by encode and
+    by decode: inputs read plus outputs written, tables excluded."""
+    d, G = w.head_dim, w.head_dim // 32
     in_b = 4 if w.dtype == "f32" else 2
     planes = d * w.v_bits // 8 + 2 * G + d * w.k_bits // 8 + 4 * G
-    enc = R * (2 * d * in_b + planes)
-    dec = R * (planes + 2 * d * 2)
-    return enc, dec
+    return 2 * d * in_b + planes, planes + 2 * d * 2
 
 
-def source_digest():
-    from kv_cache_quantization_tq_amd.build import source_digest as digest
-    return digest()
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed counter runs, if they were
     taken on the current kernel source."""
     try:
-        with open(TRAFFIC) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
+    from kv_cache_quantization_tq_amd.build import source_digest
     if t.get("source_sha256") != source_digest():
         return None
     k = t.get("kernels", {}).get(kernel)
@@ -88,27 +119,254 @@ def device_copy_gbps(torch, dev, mib=256, nbuf=6, reps=20):
     return 2 * mib * 2 ** 20 / t / 1e9
 
 
-def cpu_baseline(w, k, v):
-    import oracle as O
-    from kv_cache_quantization_tq_amd import workloads as W
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, single thread and on all host threads
+# ---------------------------------------------------------------------------
 
-    kn, vn = W.to_oracle(k), W.to_oracle(v)
-    t0 = time.perf_counter()
-    planes = O.encode_kv(kn, vn, head_dim=w.head_dim, k_bits=w.k_bits, v_bits=w.v_bits, k_signed=w.k_signed)
-    t1 = time.perf_counter()
-    O.decode_kv(planes, rows=w.rows, head_dim=w.head_dim, k_bits=w.k_bits, v_bits=w.v_bits, k_signed=w.k_signed)
-    t2 = time.perf_counter()
-    log(f"cpu oracle: encode {t1 - t0:.2f} s, decode {t2 - t1:.2f} s for {w.rows} rows")
-    return {"value": w.kv_tokens / (t2 - t0), "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole workload, one pass: encode + decode of {w.rows} rows "
-                      f"({w.kv_tokens} tokens x {w.heads} heads), single thread"}
+def _oracle_threads():
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _par(fn, rows, threads):
+    """Run fn(r0, r1) over `threads` contiguous row ranges at once (the
+    oracle's C calls release the GIL)."""
+    if threads == 1:
+        fn(0, rows)
+        return
+    cuts = [rows * i // threads for i in range(threads + 1)]
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda i: fn(cuts[i], cuts[i + 1]), range(threads)))
+
+
+def cpu_baseline(w, kn, vn, do_encode, do_decode, tokens_per_row):
+    """Oracle throughput on host rows kn, vn ([rows, d] numpy, the workload's
+    input dtype): time of encode and/or decode over those rows, single
+    thread and on all threads, scaled to KV tokens/s."""
+    import oracle as O
+
+    d = w.head_dim
+    rows = kn.reshape(-1, d).shape[0]
+    kn, vn = kn.reshape(rows, d), vn.reshape(rows, d)
+    args = dict(head_dim=d, k_bits=w.k_bits, v_bits=w.v_bits, k_signed=w.k_signed)
+    planes = O.encode_kv(kn, vn, **args)  # decode input (untimed when only decode is measured)
+    O.decode_kv({n: p[:64] for n, p in planes.items()}, rows=64, **args)  # warm-up, untimed
+
+    def run(threads):
+        def enc(r0, r1):
+            O.encode_kv(kn[r0:r1], vn[r0:r1], **args)
+
+        def dec(r0, r1):
+            O.decode_kv({n: p[r0:r1] for n, p in planes.items()}, rows=r1 - r0, **args)
+
+        t0 = time.perf_counter()
+        if do_encode:
+            _par(enc, rows, threads)
+        if do_decode:
+            _par(dec, rows, threads)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nt = _oracle_threads()
+    tn = run(nt) if nt > 1 else t1
+    kv_tok = rows * tokens_per_row
+    what = " + ".join(s for s, on in (("encode", do_encode), ("decode", do_decode)) if on)
+    log(f"cpu oracle ({what}, {rows} rows): 1 thread {t1:.2f} s, {nt} threads {tn:.2f} s")
+    return {"value": kv_tok / tn, "unit": "KV tokens/s", "cores": nt, "kind": "oracle",
+            "value_1_thread": kv_tok / t1,
+            "sample": f"{what} of {rows} rows ({rows // w.heads} tokens x {w.heads} heads) of this workload, "
+                      f"rows split over {nt} threads (single-thread figure alongside)"}
+
+
+# ---------------------------------------------------------------------------
+# Workload steps
+# ---------------------------------------------------------------------------
+
+class HipEvent:
+    """A timing event created with hipEventDisableSystemFence: recording it
+    performs no system-scope cache write-back and invalidation, which would
+    otherwise add several microseconds to every marked step and slow the
+    kernel that follows. Calls go to the HIP runtime already loaded in the
+    process (the one the codec library and torch use)."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for ln in f:
+                    if "libamdhip64" in ln:
+                        path = ln.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded in this process")
+            L = ctypes.CDLL(path)
+            P = ctypes.c_void_p
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [P, P]
+            L.hipEventSynchronize.argtypes = [P]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+            L.hipEventDestroy.argtypes = [P]
+            cls._hip = L
+        return cls._hip
+
+    def __init__(self, stream):
+        import ctypes
+        self._c = ctypes
+        self.stream = stream
+        self.ev = ctypes.c_void_p()
+        if self.hip().hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self):
+        if self.hip().hipEventRecord(self.ev, self.stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both complete)."""
+        ms = self._c.c_float()
+        if self.hip().hipEventSynchronize(end.ev) != 0 or \
+                self.hip().hipEventElapsedTime(self._c.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
+class Timer:
+    """Events on the launch stream over the timed loop: ev[i][0] marks the
+    start of step i (and the end of step i - 1), ev[i][m] for m >= 1 the
+    boundaries between the step's kernels; ev[steps][0] ends the loop. A
+    kernel is a pair (a, b) of mark indices, b == marks meaning the next
+    step's start."""
+
+    def __init__(self, torch, steps, marks):
+        stream = ctypes_stream(torch)
+        self.marks = marks
+        self.ev = [[HipEvent(stream) for _ in range(marks)] for _ in range(steps)] + [[HipEvent(stream)]]
+
+    @property
+    def start(self):
+        return self.ev[0][0]
+
+    @property
+    def end(self):
+        return self.ev[-1][0]
+
+    def per_kernel_ms(self, a, b):
+        out = []
+        for i in range(len(self.ev) - 1):
+            e1 = self.ev[i + 1][0] if b == self.marks else self.ev[i][b]
+            out.append(self.ev[i][a].elapsed_time(e1))
+        return out
+
+
+def ctypes_stream(torch):
+    """The current torch stream as the hipStream_t the codec is launched on."""
+    return torch.cuda.current_stream().cuda_stream
+
+
+def setup_encode_decode(torch, tq, W, w, dev, sets_hint):
+    """Rotating buffer sets for an encode-all + decode-all step."""
+    k0, v0 = W.make_kv(w, dev)
+    enc_b, _ = row_bytes(w)
+    per_set = w.rows * (enc_b + 2 * w.head_dim * 2 * 2)
+    nsets = sets_hint or max(2, math.ceil(1.5 * 2 ** 30 / per_set))
+    sets = []
+    for s in range(nsets):
+        k = k0 if s == 0 else k0.clone()
+        v = v0 if s == 0 else v0.clone()
+        planes = tq.empty_planes(w.rows, w.head_dim, w.k_bits, w.v_bits, dev)
+        sets.append((k, v, planes, torch.empty_like(k, dtype=torch.bfloat16),
+                     torch.empty_like(v, dtype=torch.bfloat16)))
+    log(f"workload {w.name}: {w.rows} rows, {nsets} buffer sets of {per_set / 2**20:.0f} MiB")
+
+    def step(i, ev=None):
+        k, v, planes, ko, vo = sets[i % nsets]
+        if ev is not None:
+            ev[0].record()
+        tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed, out=planes)
+        if ev is not None:
+            ev[1].record()
+        tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
+                     k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
+
+    enc_b, dec_b = row_bytes(w)
+    kernels = {"encode": (0, 1, w.rows * enc_b), "decode": (1, 2, w.rows * dec_b)}
+    tokens = lambda i: w.kv_tokens
+    host = lambda: (W.to_oracle(k0), W.to_oracle(v0))
+    return step, 2, kernels, tokens, host, {"buffer_sets": nsets}
+
+
+def setup_long_decode(torch, tq, W, w, dev, max_steps):
+    """A cache of w.tokens tokens with room for max_steps appends."""
+    T, H, d = w.tokens, w.heads, w.head_dim
+    k, v = W.make_kv(w, dev)
+    planes = tq.empty_planes((T + max_steps) * H, d, w.k_bits, w.v_bits, dev)
+    head = {n: p[: T * H] for n, p in planes.items()}
+    tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, out=head)
+    torch.cuda.synchronize()
+    sample = (W.to_oracle(k[:32768]), W.to_oracle(v[:32768]))
+    del k, v
+    appends = [W.append_token(w, s, dev) for s in range(max_steps)]
+    ko = torch.empty(((T + max_steps), H, d), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    row_b = {n: p.shape[1] * p.element_size() for n, p in planes.items()}
+    log(f"workload {w.name}: {T} cached tokens x {H} heads, room for {max_steps} appends")
+
+    def step(i, ev=None):
+        n = T + i  # tokens already cached
+        view = {nm: p[n * H:(n + 1) * H] for nm, p in planes.items()}
+        nk, nv = appends[i]
+        if ev is not None:
+            ev[0].record()
+        tq.encode_kv(nk, nv, v_bits=w.v_bits, k_bits=w.k_bits, out=view)
+        if ev is not None:
+            ev[1].record()
+        tq.decode_kv(planes, tokens=n + 1, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits,
+                     k_out=ko[: n + 1], v_out=vo[: n + 1])
+
+    enc_b, dec_b = row_bytes(w)
+    # decode bytes of the first timed step's cache length (the cache grows by
+    # one token per step: under 0.05% over a run)
+    kernels = {"append": (0, 1, H * enc_b), "decode": (1, 2, (T + 1) * H * dec_b)}
+    tokens = lambda i: T + i + 1
+    return step, 2, kernels, tokens, (lambda: sample), {"cached_tokens": T, "appended_per_step": 1}
+
+
+def setup_joint(torch, tq, W, w, dev):
+    k, v = W.make_kv(w, dev)
+    planes = tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits)
+    torch.cuda.synchronize()
+    ns = 16384 * w.heads  # rows of the oracle sample: the first 16384 tokens
+    sample = (W.to_oracle(k.view(-1, w.head_dim)[:ns]), W.to_oracle(v.view(-1, w.head_dim)[:ns]))
+    del k, v
+    ko = torch.empty((w.kv_tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    log(f"workload {w.name}: {w.rows} rows")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
+                     k_bits=w.k_bits, k_out=ko, v_out=vo)
+
+    _, dec_b = row_bytes(w)
+    return step, 1, {"decode": (0, 1, w.rows * dec_b)}, (lambda i: w.kv_tokens), (lambda: sample), {}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (0: 50, or 20 for the decode workloads)")
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=sorted(DESCRIPTION))
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for >= 1.5 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -130,33 +388,17 @@ def main():
         sys.exit(1)
     tq.lib()
     dev = torch.device("cuda:0")
-    w = W.WORKLOADS["prefill"]
-    enc_bytes, dec_bytes = algorithmic_bytes(w)
-    k0, v0 = W.make_kv(w, dev)
-    per_set = 2 * k0.numel() * k0.element_size() * 2 + enc_bytes - 2 * k0.numel() * k0.element_size()
-    nsets = args.sets or max(2, math.ceil(1.5 * 2 ** 30 / per_set))
-    sets = []
-    for s in range(nsets):
-        k = k0 if s == 0 else k0.clone()
-        v = v0 if s == 0 else v0.clone()
-        planes = tq.empty_planes(w.rows, w.head_dim, w.k_bits, w.v_bits, dev)
-        ko = torch.empty_like(k)
-        vo = torch.empty_like(v)
-        sets.append((k, v, planes, ko, vo))
-    torch.cuda.synchronize()
-    log(f"workload prefill: {w.rows} rows, {nsets} buffer sets of {per_set / 2**20:.0f} MiB")
+    w = W.WORKLOADS[args.workload]
+    steps = args.steps or (20 if args.workload in ("long_decode", "joint_large") else 50)
 
-    def step(i, ev=None):
-        k, v, planes, ko, vo = sets[i % nsets]
-        if ev is not None:
-            ev[0].record()
-        tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed, out=planes)
-        if ev is not None:
-            ev[1].record()
-        tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
-                     k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
-        if ev is not None:
-            ev[2].record()
+    if args.workload in ("prefill", "small_head"):
+        step, marks, kernels, tokens, host, extra = setup_encode_decode(torch, tq, W, w, dev, args.sets)
+    elif args.workload == "long_decode":
+        step, marks, kernels, tokens, host, extra = setup_long_decode(torch, tq, W, w, dev,
+                                                                      args.warmup + steps)
+    else:
+        step, marks, kernels, tokens, host, extra = setup_joint(torch, tq, W, w, dev)
+    torch.cuda.synchronize()
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 2 ** 20 // 4
@@ -172,55 +414,46 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # whole-step timing
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed region: exactly `steps` steps, with events between kernels
+    tm = Timer(torch, steps, marks)
     torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(i)
-    t_end.record()
+    for i in range(steps):
+        step(args.warmup + i, tm.ev[i])
+    tm.end.record()
     torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = tm.start.elapsed_time(tm.end) / steps
+    kv_tokens = sum(tokens(args.warmup + i) for i in range(steps))
 
-    # per-kernel durations (events on the stream the kernels are launched on)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    enc_avg = sum(enc_ms) / len(enc_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    enc_gbps = enc_bytes / (enc_avg * 1e-3) / 1e9
-    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
-    log(f"encode: avg {enc_avg * 1e3:.1f} us  median {enc_ms[len(enc_ms) // 2] * 1e3:.1f} us  "
-        f"{enc_gbps:.0f} GB/s ({enc_gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s)")
-    log(f"decode: avg {dec_avg * 1e3:.1f} us  median {dec_ms[len(dec_ms) // 2] * 1e3:.1f} us  "
-        f"{dec_gbps:.0f} GB/s ({dec_gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s)")
-    log(f"step: {ms_per_step * 1e3:.1f} us")
-
-    # context: a plain device-to-device copy of the same size class on this GPU
+    stats = {}
+    for name, (a, b, nbytes) in kernels.items():
+        ms = sorted(tm.per_kernel_ms(a, b))
+        avg = sum(ms) / len(ms)
+        gbps = nbytes / (avg * 1e-3) / 1e9
+        stats[name] = {"avg_us": avg * 1e3, "median_us": ms[len(ms) // 2] * 1e3, "GBps": gbps,
+                       "bytes": nbytes, "frac": gbps / PEAK_HBM_GBPS}
+        log(f"{name}: avg {avg * 1e3:.1f} us  median {ms[len(ms) // 2] * 1e3:.1f} us  "
+            f"{gbps:.0f} GB/s ({gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s)")
+    step_bytes = sum(v[2] for v in kernels.values())
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     copy_gbps = device_copy_gbps(torch, dev)
-    step_gbps = (enc_bytes + dec_bytes) / (ms_per_step * 1e-3) / 1e9
-    log(f"whole step: {step_gbps:.0f} GB/s ({step_gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s); "
+    log(f"step: {ms_per_step * 1e3:.1f} us, {step_gbps:.0f} GB/s ({step_gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s); "
         f"device copy reference {copy_gbps:.0f} GB/s")
 
-    if enc_avg >= dec_avg:
-        kern, nbytes, avg, gbps = "encode", enc_bytes, enc_avg, enc_gbps
-    else:
-        kern, nbytes, avg, gbps = "decode", dec_bytes, dec_avg, dec_gbps
-
+    dom = max(stats, key=lambda n: stats[n]["avg_us"])
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, k0, v0)
+        kn, vn = host()
+        if args.workload in ("prefill", "small_head"):
+            cpu = cpu_baseline(w, kn, vn, True, True, 1.0 / w.heads)
+        else:
+            cpu = cpu_baseline(w, kn, vn, False, True, 1.0 / w.heads)
 
     out = {
-        "metric": METRIC,
-        "value": w.kv_tokens / (ms_per_step * 1e-3),
+        "metric": METRIC[args.workload],
+        "value": kv_tokens / (steps * ms_per_step * 1e-3),
         "unit": "KV tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
@@ -228,17 +461,14 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "prefill: batch 1, 8 KV heads, head_dim 128, 32768 tokens, bf16 K/V "
-                               "(N(0,1) x per-channel log-uniform [0.1,10] scales); values 4-bit Lloyd-Max, "
-                               "keys 4-bit affine; encode all + decode all to bf16",
-                   "tokens": w.kv_tokens, "heads": w.heads, "head_dim": w.head_dim, "v_bits": w.v_bits,
-                   "k_bits": w.k_bits, "input_dtype": w.dtype, "buffer_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": kern, "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": gbps / PEAK_HBM_GBPS, "traffic": measured_traffic(kern),
-                     "algorithmic_bytes": nbytes, "avg_kernel_us": avg * 1e3},
-        "kernels": {"encode": {"avg_us": enc_avg * 1e3, "GBps": enc_gbps, "bytes": enc_bytes},
-                    "decode": {"avg_us": dec_avg * 1e3, "GBps": dec_gbps, "bytes": dec_bytes},
-                    "step": {"GBps": step_gbps, "frac": step_gbps / PEAK_HBM_GBPS},
+        "config": {"workload": DESCRIPTION[args.workload], "tokens": w.kv_tokens, "heads": w.heads,
+                   "head_dim": w.head_dim, "v_bits": w.v_bits, "k_bits": w.k_bits,
+                   "k_signed": w.k_signed, "input_dtype": w.dtype, **extra},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": stats[dom]["GBps"], "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": stats[dom]["GBps"] / PEAK_HBM_GBPS,
+                     "traffic": measured_traffic(args.workload, dom),
+                     "algorithmic_bytes": stats[dom]["bytes"], "avg_kernel_us": stats[dom]["avg_us"]},
+        "kernels": {**stats, "step": {"GBps": step_gbps, "frac": step_gbps / PEAK_HBM_GBPS},
                     "device_copy_reference_GBps": copy_gbps},
         "cpu_baseline": cpu,
     }

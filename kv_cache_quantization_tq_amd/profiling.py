@@ -1,11 +1,12 @@
 """Summaries of rocprofv3 output for the codec kernels.
 
-    python -m kv_cache_quantization_tq_amd.profiling trace <kernel_trace.csv>
+    python -m kv_cache_quantization_tq_amd.profiling trace <kernel_trace.csv> [--stats <kernel_stats.csv>]
     python -m kv_cache_quantization_tq_amd.profiling traffic <fetch.csv> <write.csv> \
         --copy-mib 512 [--json out.json]
 
 ``trace`` prints per-kernel dispatch counts and average / median / min
-durations from a ``--kernel-trace`` CSV. ``traffic`` turns the FETCH_SIZE and
+durations from a ``--kernel-trace`` CSV, and with ``--stats`` the codec
+kernels' rows of rocprofv3's own ``--stats`` table. ``traffic`` turns the FETCH_SIZE and
 WRITE_SIZE counters (KiB per dispatch) of two ``--pmc`` runs of
 ``bench.py --copy-calibration-mib N`` into HBM bytes per launch: each
 counter is scaled by the factor that maps the same counter, read on the
@@ -62,6 +63,17 @@ def trace_summary(path: str) -> str:
     return "\n".join(lines)
 
 
+def stats_summary(path: str) -> str:
+    lines = [f"{'kernel (rocprofv3 --stats)':70s} {'calls':>5s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s}"]
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = short_name(r["Name"])
+            if kernel_kind(name) in ("encode", "decode", "unrotate"):
+                lines.append(f"{name[:70]:70s} {int(r['Calls']):5d} {float(r['AverageNs']) * 1e-3:8.2f} "
+                             f"{float(r['MinNs']) * 1e-3:8.2f} {float(r['MaxNs']) * 1e-3:8.2f}")
+    return "\n".join(lines)
+
+
 def read_counter(path: str, counter: str):
     out = {}
     with open(path) as f:
@@ -104,6 +116,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("csv")
+    t.add_argument("--stats")
     c = sub.add_parser("traffic")
     c.add_argument("fetch_csv")
     c.add_argument("write_csv")
@@ -112,6 +125,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace_summary(a.csv))
+        if a.stats:
+            print()
+            print(stats_summary(a.stats))
     else:
         res = traffic(a.fetch_csv, a.write_csv, a.copy_mib)
         txt = json.dumps(res, indent=1)

@@ -145,6 +145,59 @@ int32_t tq_sign_vector(int32_t head_dim, float *signs);
  * checking the search on the CPU. Host only. */
 int32_t tq_value_bin_host(int32_t bits, const float *z, int64_t n, uint8_t *idx);
 
+/* ---------------------------------------------------------------------
+ * Token-axis batching of packed caches (page "mlx-bun 0.0.9 -> 0.0.11",
+ * src/model/batched-quant.ts: mergeQuantRows, extendQuantRows,
+ * extractQuantRow, filterQuantRows). Codec groups run along head_dim only,
+ * so moving whole tokens is byte-exact: a sequence's bytes come out exactly
+ * as they were encoded.
+ *
+ * A batch of b sequences of width W is a plane set of b * W tokens (each
+ * token `heads` rows of every plane), sequence-major: sequence s occupies
+ * tokens [s * W, (s + 1) * W). Sequences are left-padded: a sequence of L
+ * tokens sits in the last L token slots of its W and the W - L slots before
+ * it hold zero bytes in every plane (they decode to zeros; callers mask
+ * them out of attention). left_pad[s] = W - L.
+ *
+ * The planes handled are the members of `dst` that are not NULL (keys only,
+ * values only, or all five); every source must have those planes. `cfg`
+ * gives the row sizes (head_dim, k_bits, v_bits; k_signed as for the
+ * codec). Source and destination must not overlap. Any alignment is
+ * accepted. Arrays named lens / left_pad* / keep are host memory; planes
+ * are device memory; `srcs`, `batch`, `row`, `dst` are host structs. A
+ * call whose output holds no tokens touches no plane pointer; planes of a
+ * source that contributes no tokens may be NULL. Errors (TQ_E_*) are
+ * returned before any launch and leave dst untouched.
+ * --------------------------------------------------------------------- */
+
+/* mergeQuantRows: stack n caches (srcs[i] holds lens[i] tokens) into dst,
+ * a batch of n sequences of width `width` >= max(lens) (the page uses the
+ * maximum; a larger width pads every sequence further). Writes
+ * left_pad[i] = width - lens[i] when left_pad is not NULL. */
+int32_t tq_merge_rows(const tq_packed_kv *srcs, const int64_t *lens, int32_t n, int64_t width, int32_t heads,
+                      const tq_config *cfg, const tq_packed_kv *dst, int64_t *left_pad, void *stream);
+
+/* extendQuantRows: append one cache `row` of row_len tokens to `batch`
+ * (b sequences of width `width`, left pads left_pad_in) as sequence b of
+ * dst, a batch of b + 1 sequences of width new_width >= max(width,
+ * row_len). Existing pads grow by new_width - width; the new sequence's pad
+ * is new_width - row_len (written to left_pad_out when it is not NULL;
+ * left_pad_in is then required if b > 0). b may be 0 (batch unused). */
+int32_t tq_extend_rows(const tq_packed_kv *batch, int32_t b, int64_t width, const int64_t *left_pad_in,
+                       const tq_packed_kv *row, int64_t row_len, int64_t new_width, int32_t heads,
+                       const tq_config *cfg, const tq_packed_kv *dst, int64_t *left_pad_out, void *stream);
+
+/* extractQuantRow: copy sequence i of `batch` (b sequences of width
+ * `width`) past its left pad into dst, a cache of width - left_pad tokens. */
+int32_t tq_extract_row(const tq_packed_kv *batch, int32_t b, int64_t width, int32_t i, int64_t left_pad,
+                       int32_t heads, const tq_config *cfg, const tq_packed_kv *dst, void *stream);
+
+/* filterQuantRows: dst sequence j = batch sequence keep[j] (0 <= keep[j] <
+ * b), j < n; widths unchanged. The page keeps sorted indices; any valid
+ * indices are accepted here. */
+int32_t tq_filter_rows(const tq_packed_kv *batch, int32_t b, int64_t width, const int32_t *keep, int32_t n,
+                       int32_t heads, const tq_config *cfg, const tq_packed_kv *dst, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,6 +33,7 @@ TQ_DECODE_ROTATED_V = 1
 EXPORTS = (
     "tq_packed_dim", "tq_status_string", "tq_encode_kv", "tq_decode_kv", "tq_unrotate_values",
     "tq_lloyd_max_table", "tq_sign_vector", "tq_value_bin_host",
+    "tq_merge_rows", "tq_extend_rows", "tq_extract_row", "tq_filter_rows",
 )
 
 
@@ -73,6 +74,14 @@ def lib() -> ctypes.CDLL:
             "tq_lloyd_max_table": (i32, [i32, P, P]),
             "tq_sign_vector": (i32, [i32, P]),
             "tq_value_bin_host": (i32, [i32, P, i64, P]),
+            "tq_merge_rows": (i32, [ctypes.POINTER(TQPackedKV), P, i32, i64, i32, ctypes.POINTER(TQConfig),
+                                    ctypes.POINTER(TQPackedKV), P, P]),
+            "tq_extend_rows": (i32, [ctypes.POINTER(TQPackedKV), i32, i64, P, ctypes.POINTER(TQPackedKV), i64,
+                                     i64, i32, ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P, P]),
+            "tq_extract_row": (i32, [ctypes.POINTER(TQPackedKV), i32, i64, i32, i64, i32,
+                                     ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
+            "tq_filter_rows": (i32, [ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
+                                     ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -245,3 +254,83 @@ def unrotate_values(x, out=None, stream=None):
     if st:
         raise TQError(st, "tq_unrotate_values")
     return out
+
+
+# ------------------------------------------------- token-axis batching ops
+#
+# Plane dicts as above; a batch of b sequences of width W holds b * W tokens
+# (b * W * heads rows per plane). The planes handled are those present in
+# the source dicts; outputs are allocated with the same set.
+
+def _like(planes: Dict, tokens: int, heads: int, head_dim: int, k_bits: int, v_bits: int):
+    ref = next(p for p in planes.values() if p is not None)
+    full = empty_planes(tokens * heads, head_dim, k_bits, v_bits, ref.device)
+    return {n: full[n] for n in planes}
+
+
+def _i64(vals):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(vals, dtype=np.int64))
+
+
+def merge_rows(caches, lens, *, heads: int, head_dim: int, k_bits: int, v_bits: int, k_signed: bool = False,
+               width: Optional[int] = None, stream=None):
+    """Stack caches (plane dicts, cache i holding lens[i] tokens) into one
+    left-padded batch. Returns (planes, left_pad, width)."""
+    n = len(caches)
+    lens_a = _i64(lens)
+    width = int(lens_a.max()) if width is None and n else int(width or 0)
+    dst = _like(caches[0], n * width, heads, head_dim, k_bits, v_bits)
+    srcs = (TQPackedKV * max(n, 1))(*[_packed(c) for c in caches])
+    pad = _i64([0] * max(n, 1))
+    cfg = TQConfig(head_dim, k_bits, v_bits, int(bool(k_signed)))
+    st = lib().tq_merge_rows(srcs, lens_a.ctypes.data, n, width, heads, ctypes.byref(cfg),
+                             ctypes.byref(_packed(dst)), pad.ctypes.data, _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_merge_rows")
+    return dst, [int(x) for x in pad[:n]], width
+
+
+def extend_rows(batch, b: int, width: int, left_pad, row, row_len: int, *, heads: int, head_dim: int,
+                k_bits: int, v_bits: int, k_signed: bool = False, new_width: Optional[int] = None, stream=None):
+    """Append cache `row` (row_len tokens) to a batch of b sequences of width
+    `width`. Returns (planes, left_pad, new_width)."""
+    new_width = max(width, row_len) if new_width is None else int(new_width)
+    dst = _like(row, (b + 1) * new_width, heads, head_dim, k_bits, v_bits)
+    pin = _i64(list(left_pad) + [0])
+    pout = _i64([0] * (b + 1))
+    cfg = TQConfig(head_dim, k_bits, v_bits, int(bool(k_signed)))
+    bp = _packed(batch) if batch is not None else TQPackedKV()
+    st = lib().tq_extend_rows(ctypes.byref(bp), b, width, pin.ctypes.data, ctypes.byref(_packed(row)), row_len,
+                              new_width, heads, ctypes.byref(cfg), ctypes.byref(_packed(dst)), pout.ctypes.data,
+                              _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_extend_rows")
+    return dst, [int(x) for x in pout], new_width
+
+
+def extract_row(batch, b: int, width: int, i: int, left_pad: int, *, heads: int, head_dim: int, k_bits: int,
+                v_bits: int, k_signed: bool = False, stream=None):
+    """Sequence i of a batch, past its left pad, as a cache of width - left_pad tokens."""
+    dst = _like(batch, width - left_pad, heads, head_dim, k_bits, v_bits)
+    cfg = TQConfig(head_dim, k_bits, v_bits, int(bool(k_signed)))
+    st = lib().tq_extract_row(ctypes.byref(_packed(batch)), b, width, i, left_pad, heads, ctypes.byref(cfg),
+                              ctypes.byref(_packed(dst)), _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_extract_row")
+    return dst
+
+
+def filter_rows(batch, b: int, width: int, keep, *, heads: int, head_dim: int, k_bits: int, v_bits: int,
+                k_signed: bool = False, stream=None):
+    """Sequences keep[j] of a batch, in that order, as a batch of len(keep)."""
+    import numpy as np
+    keep_a = np.ascontiguousarray(np.asarray(keep, dtype=np.int32))
+    dst = _like(batch, len(keep_a) * width, heads, head_dim, k_bits, v_bits)
+    cfg = TQConfig(head_dim, k_bits, v_bits, int(bool(k_signed)))
+    st = lib().tq_filter_rows(ctypes.byref(_packed(batch)), b, width, keep_a.ctypes.data if keep_a.size else None,
+                              len(keep_a), heads, ctypes.byref(cfg), ctypes.byref(_packed(dst)),
+                              _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_filter_rows")
+    return dst

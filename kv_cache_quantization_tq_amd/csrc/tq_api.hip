@@ -1,6 +1,8 @@
-// tq_api.hip -- host side of the TurboQuant KV-cache codec: the C ABI declared
-// in include/tq.h (argument validation, grid sizing, launches) and the host
-// copies of the tables. The kernels live in tq_kernels_d<head_dim>.hip.
+// tq_api.hip -- host side of the TurboQuant KV-cache codec: the codec part of
+// the C ABI declared in include/tq.h (argument validation, grid sizing,
+// launches) and the host copies of the tables. The kernels live in
+// tq_kernels_d<head_dim>.hip; the token-axis batching operations in
+// tq_batch.hip.
 #include <hip/hip_runtime.h>
 
 #include <stdlib.h>
@@ -11,13 +13,16 @@
 #include "tq.h"
 #include "tq_device.h"
 #include "tq_dispatch.h"
+#include "tq_host.h"
 
 namespace {
 
-bool valid_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
-bool valid_bits(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 8; }
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-uintptr_t code_align(int32_t bits) { return (bits == 4 || bits == 8) ? 16 : 8; }
+using tq_host::aligned;
+using tq_host::check_rows;
+using tq_host::code_align;
+using tq_host::valid_bits;
+using tq_host::valid_head_dim;
+using tq_host::valid_key_cfg;
 
 // Persistent grid: as many blocks as can be resident at once (occupancy of
 // the kernel times the device's compute units), capped by the number of
@@ -58,14 +63,6 @@ int64_t grid_for(const void *fn, int64_t rows, int32_t d)
     const int64_t resident = (int64_t)per_cu * ncu;
     if (blocks > resident) blocks = resident;
     return blocks < 1 ? 1 : blocks;
-}
-
-int32_t check_rows(int64_t tokens, int32_t heads, int64_t *rows)
-{
-    if (tokens < 0 || heads < 1) return TQ_E_SHAPE;
-    if (tokens > (int64_t)1 << 40 || heads > (1 << 20)) return TQ_E_SHAPE;
-    *rows = tokens * heads;
-    return TQ_OK;
 }
 
 int32_t key_mode(const tq_config *cfg) { return cfg->k_bits | (cfg->k_signed ? 16 : 0); }
@@ -155,9 +152,7 @@ int32_t tq_encode_kv(const void *k, const void *v, int32_t in_dtype, int64_t tok
     if (rows == 0) return TQ_OK;
     if (k == nullptr && v == nullptr) return TQ_E_NULL;
     if (k != nullptr) {
-        if (!valid_bits(cfg->k_bits) || (cfg->k_signed != 0 && cfg->k_bits != 8) ||
-            (cfg->k_signed != 0 && cfg->k_signed != 1))
-            return TQ_E_BITS;
+        if (!valid_key_cfg(cfg)) return TQ_E_BITS;
         if (out->k_codes == nullptr || out->k_scale == nullptr || out->k_zero == nullptr) return TQ_E_NULL;
         if (!aligned(k, 16) || !aligned(out->k_codes, code_align(cfg->k_bits)) || !aligned(out->k_scale, 2) ||
             !aligned(out->k_zero, 2))
@@ -192,9 +187,7 @@ int32_t tq_decode_kv(const tq_packed_kv *in, int64_t tokens, int32_t heads, cons
     if (rows == 0) return TQ_OK;
     if (k_out == nullptr && v_out == nullptr) return TQ_E_NULL;
     if (k_out != nullptr) {
-        if (!valid_bits(cfg->k_bits) || (cfg->k_signed != 0 && cfg->k_bits != 8) ||
-            (cfg->k_signed != 0 && cfg->k_signed != 1))
-            return TQ_E_BITS;
+        if (!valid_key_cfg(cfg)) return TQ_E_BITS;
         if (in->k_codes == nullptr || in->k_scale == nullptr || in->k_zero == nullptr) return TQ_E_NULL;
         if (!aligned(k_out, 16) || !aligned(in->k_codes, code_align(cfg->k_bits)) || !aligned(in->k_scale, 2) ||
             !aligned(in->k_zero, 2))

@@ -159,3 +159,45 @@ def test_kernel_bin_search_equals_oracle_count(bits):
     z = np.concatenate(z)
     z = z[~np.isnan(z)]
     np.testing.assert_array_equal(tq.value_bin_host(bits, z), O.bin_index(z, bits))
+
+
+def _pk(vals):
+    return tq.TQPackedKV(*vals)
+
+
+def test_batching_argument_validation():
+    L = tq.lib()
+    cfg = tq.TQConfig(128, 4, 4, 0)
+    dst = _pk([FAKE] * 5)
+    srcs = (tq.TQPackedKV * 2)(_pk([FAKE] * 5), _pk([FAKE] * 5))
+    lens = (ctypes.c_int64 * 2)(3, 5)
+    by = ctypes.byref
+    # merge
+    assert L.tq_merge_rows(srcs, lens, 2, 4, 2, by(cfg), by(dst), None, None) == tq.TQ_E_SHAPE   # width < len
+    assert L.tq_merge_rows(srcs, lens, -1, 5, 2, by(cfg), by(dst), None, None) == tq.TQ_E_SHAPE
+    assert L.tq_merge_rows(srcs, lens, 0, 5, 2, by(cfg), by(dst), None, None) == tq.TQ_OK       # nothing to do
+    assert L.tq_merge_rows(srcs, lens, 2, 5, 0, by(cfg), by(dst), None, None) == tq.TQ_E_SHAPE   # heads
+    assert L.tq_merge_rows(srcs, lens, 2, 5, 2, by(tq.TQConfig(96, 4, 4, 0)), by(dst), None, None) == tq.TQ_E_HEAD_DIM
+    assert L.tq_merge_rows(srcs, lens, 2, 5, 2, by(tq.TQConfig(128, 6, 4, 0)), by(dst), None, None) == tq.TQ_E_BITS
+    # values only: the key bits are not checked
+    vdst = _pk([None, None, None, FAKE, FAKE])
+    assert L.tq_merge_rows(srcs, lens, 0, 5, 2, by(tq.TQConfig(128, 6, 4, 0)), by(vdst), None, None) == tq.TQ_OK
+    assert L.tq_merge_rows(srcs, lens, 2, 5, 2, by(cfg), by(_pk([None] * 5)), None, None) == tq.TQ_E_NULL
+    nsrcs = (tq.TQPackedKV * 2)(_pk([FAKE] * 5), _pk([FAKE, FAKE, None, FAKE, FAKE]))
+    assert L.tq_merge_rows(nsrcs, lens, 2, 5, 2, by(cfg), by(dst), None, None) == tq.TQ_E_NULL
+    # extend
+    row = _pk([FAKE] * 5)
+    pin = (ctypes.c_int64 * 2)(0, 2)
+    pout = (ctypes.c_int64 * 3)()
+    assert L.tq_extend_rows(by(dst), 2, 5, pin, by(row), 7, 6, 2, by(cfg), by(dst), pout, None) == tq.TQ_E_SHAPE
+    assert L.tq_extend_rows(by(dst), 2, 5, None, by(row), 3, 5, 2, by(cfg), by(dst), pout, None) == tq.TQ_E_NULL
+    assert L.tq_extend_rows(by(dst), -1, 5, pin, by(row), 3, 5, 2, by(cfg), by(dst), pout, None) == tq.TQ_E_SHAPE
+    # extract
+    assert L.tq_extract_row(by(dst), 2, 5, 2, 0, 2, by(cfg), by(dst), None) == tq.TQ_E_SHAPE    # i >= b
+    assert L.tq_extract_row(by(dst), 2, 5, 0, 6, 2, by(cfg), by(dst), None) == tq.TQ_E_SHAPE    # pad > width
+    assert L.tq_extract_row(by(dst), 0, 5, 0, 0, 2, by(cfg), by(dst), None) == tq.TQ_E_SHAPE
+    # filter
+    keep = (ctypes.c_int32 * 2)(0, 2)
+    assert L.tq_filter_rows(by(dst), 2, 5, keep, 2, 2, by(cfg), by(dst), None) == tq.TQ_E_SHAPE  # keep[1] >= b
+    assert L.tq_filter_rows(by(dst), 2, 5, None, 2, 2, by(cfg), by(dst), None) == tq.TQ_E_NULL
+    assert L.tq_filter_rows(by(dst), 2, 5, None, 0, 2, by(cfg), by(dst), None) == tq.TQ_OK

@@ -1,0 +1,125 @@
+"""GPU parity of the token-axis batching operations (tq_merge_rows,
+tq_extend_rows, tq_extract_row, tq_filter_rows through the C ABI) against
+the batching oracle. The operations move bytes, so the plane contents are
+seeded random bytes (any bytes are a valid input) and the bar is byte
+equality of every output plane."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_quantization_tq_amd as tq
+from oracle import batching as B
+
+pytestmark = pytest.mark.gpu
+
+CFGS = [  # head_dim, k_bits, v_bits, k_signed
+    (64, 3, 2, False),    # 24- and 16-byte code rows, 4-byte scale rows
+    (128, 4, 4, False),
+    (256, 5, 8, False),
+    (512, 8, 3, True),
+]
+SIDES = {"both": ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale"),
+         "keys": ("k_codes", "k_scale", "k_zero"), "values": ("v_codes", "v_scale")}
+HEADS = 3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tq.lib()
+    return torch.device("cuda:0")
+
+
+def host_cache(tokens, cfg, side, seed):
+    d, kb, vb, _ = cfg
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, (shape, kind) in tq.plane_shapes(tokens * HEADS, d, kb, vb).items():
+        if name not in SIDES[side]:
+            continue
+        dt = np.uint8 if kind == "uint8" else np.uint16
+        out[name] = rng.integers(0, np.iinfo(dt).max + 1, size=shape, dtype=dt)
+    return out
+
+
+def to_dev(c, dev):
+    return {n: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev) for n, a in c.items()}
+
+
+def to_host(c):
+    out = {}
+    for n, t in c.items():
+        a = t.cpu().numpy()
+        out[n] = a.view(np.uint16) if a.dtype == np.int16 else a
+    return out
+
+
+def kw(cfg):
+    d, kb, vb, ks = cfg
+    return dict(heads=HEADS, head_dim=d, k_bits=kb, v_bits=vb, k_signed=ks)
+
+
+def assert_same(got, want, what):
+    assert set(got) == set(want), what
+    for n in want:
+        assert got[n].shape == want[n].shape, (what, n, got[n].shape, want[n].shape)
+        assert np.array_equal(got[n], want[n]), f"{what}: plane {n} differs"
+
+
+LENS = [(3, 5, 2), (0, 4), (1,), (7, 7, 7), (0, 0, 3), tuple(np.random.default_rng(7).integers(0, 41, 9))]
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=lambda c: f"d{c[0]}k{c[1]}v{c[2]}")
+@pytest.mark.parametrize("side", list(SIDES))
+def test_merge_extract_filter(dev, cfg, side):
+    for li, lens in enumerate(LENS):
+        hs = [host_cache(int(n), cfg, side, 100 * li + i) for i, n in enumerate(lens)]
+        for width in (None, max(lens) + 3):
+            got, pad, w = tq.merge_rows([to_dev(h, dev) for h in hs], lens, width=width, **kw(cfg))
+            want, wpad, ww = B.merge_rows(hs, HEADS, width=width)
+            assert (pad, w) == (wpad, ww)
+            torch.cuda.synchronize()
+            g = to_host(got)
+            assert_same(g, want, f"merge {lens} width {width}")
+            b = len(lens)
+            for i in range(b):
+                e = tq.extract_row(got, b, w, i, pad[i], **kw(cfg))
+                assert_same(to_host(e), B.extract_row(want, b, w, pad[i], i, HEADS), f"extract {i} of {lens}")
+            keeps = [list(range(b)), list(range(b))[::-1], [b - 1] * 2, []]
+            for keep in keeps:
+                f = tq.filter_rows(got, b, w, keep, **kw(cfg))
+                assert_same(to_host(f), B.filter_rows(want, b, w, keep, HEADS), f"filter {keep} of {lens}")
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=lambda c: f"d{c[0]}k{c[1]}v{c[2]}")
+@pytest.mark.parametrize("side", list(SIDES))
+def test_extend(dev, cfg, side):
+    hs = [host_cache(n, cfg, side, 500 + i) for i, n in enumerate((4, 6, 1))]
+    batch_h, pad, w = B.merge_rows(hs, HEADS)
+    batch_d, _, _ = tq.merge_rows([to_dev(h, dev) for h in hs], [4, 6, 1], **kw(cfg))
+    for j, (rlen, nw) in enumerate(((2, None), (6, None), (9, None), (3, 11), (0, None))):
+        row = host_cache(rlen, cfg, side, 600 + j)
+        got, gpad, gw = tq.extend_rows(batch_d, 3, w, pad, to_dev(row, dev), rlen, new_width=nw, **kw(cfg))
+        want, wpad, ww = B.extend_rows(batch_h, 3, w, pad, row, HEADS, new_width=nw)
+        assert (gpad, gw) == (wpad, ww)
+        assert_same(to_host(got), want, f"extend by {rlen} to {nw}")
+    # from an empty batch
+    row = host_cache(5, cfg, side, 700)
+    got, gpad, gw = tq.extend_rows(None, 0, 0, [], to_dev(row, dev), 5, **kw(cfg))
+    want, wpad, ww = B.extend_rows(None, 0, 0, [], row, HEADS)
+    assert (gpad, gw) == (wpad, ww)
+    assert_same(to_host(got), want, "extend empty batch")
+
+
+def test_merge_many_sequences_large(dev):
+    """More segments than one launch holds (5 planes x 2 per sequence) and
+    multi-block segments."""
+    cfg = (128, 4, 4, False)
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(900, 2049, 30)]
+    hs = [host_cache(n, cfg, "both", 800 + i) for i, n in enumerate(lens)]
+    got, pad, w = tq.merge_rows([to_dev(h, dev) for h in hs], lens, **kw(cfg))
+    want, wpad, ww = B.merge_rows(hs, HEADS)
+    assert (pad, w) == (wpad, ww)
+    assert_same(to_host(got), want, "merge 30 sequences")

@@ -16,7 +16,10 @@ Lloyd-Max, keys 4-bit affine. What one step is:
                        (encode 8 rows at the cache's end), then decode the
                        whole cache to bf16;
 * joint_large          one joint decode of packed K and V (262144 tokens x 8
-                       heads, head_dim 512) to bf16.
+                       heads, head_dim 512) to bf16;
+* batch_merge          merge 32 packed caches of 4096..32768 tokens into one
+                       left-padded batch (the token-axis batching
+                       operation; KV tokens = tokens merged).
 
 Inputs are resident in HBM before timing starts. Prints one JSON line:
 value = KV tokens per second (one KV token = one position with K and V of
@@ -54,6 +57,8 @@ DESCRIPTION = {
                    "cache to bf16",
     "joint_large": "joint_large: batch 4 x 65536 tokens, 8 KV heads, head_dim 512, bf16 N(0,1) with 1% of "
                    "rows zeroed; values 8-bit (unpacked bytes), keys 4-bit; one joint K/V decode to bf16",
+    "batch_merge": "batch_merge: 32 packed caches (8 KV heads, head_dim 128, V4/K4 planes of seeded random "
+                   "bytes) of 4096..32768 tokens merged into one left-padded batch",
 }
 
 METRIC = {
@@ -62,6 +67,8 @@ METRIC = {
     "long_decode": "KV tokens/sec decoded per step (append 1 token + full decode, d=256, V5/K4) and "
                    "achieved HBM GB/s vs peak",
     "joint_large": "KV tokens/sec joint K/V decode (d=512, V8/K4) and achieved HBM GB/s vs peak",
+    "batch_merge": "KV tokens/sec merged into a left-padded batch (d=128, V4/K4 planes) and achieved HBM GB/s "
+                   "vs peak",
 }
 
 
@@ -91,10 +98,8 @@ def measured_traffic(workload, kernel):
     except (OSError, ValueError):
         return None
     from kv_cache_quantization_tq_amd.build import source_digest
-    if t.get("source_sha256") != source_digest():
-        return None
     k = t.get("kernels", {}).get(kernel)
-    if not k:
+    if not k or k.get("source_sha256") != source_digest(kernel):
         return None
     return int(k["fetch_bytes"] + k["write_bytes"])
 
@@ -300,8 +305,8 @@ def setup_encode_decode(torch, tq, W, w, dev, sets_hint):
     enc_b, dec_b = row_bytes(w)
     kernels = {"encode": (0, 1, w.rows * enc_b), "decode": (1, 2, w.rows * dec_b)}
     tokens = lambda i: w.kv_tokens
-    host = lambda: (W.to_oracle(k0), W.to_oracle(v0))
-    return step, 2, kernels, tokens, host, {"buffer_sets": nsets}
+    cpu = lambda: cpu_baseline(w, W.to_oracle(k0), W.to_oracle(v0), True, True, 1.0 / w.heads)
+    return step, 2, kernels, tokens, cpu, {**codec_config(w), "buffer_sets": nsets}
 
 
 def setup_long_decode(torch, tq, W, w, dev, max_steps):
@@ -337,7 +342,8 @@ def setup_long_decode(torch, tq, W, w, dev, max_steps):
     # one token per step: under 0.05% over a run)
     kernels = {"append": (0, 1, H * enc_b), "decode": (1, 2, (T + 1) * H * dec_b)}
     tokens = lambda i: T + i + 1
-    return step, 2, kernels, tokens, (lambda: sample), {"cached_tokens": T, "appended_per_step": 1}
+    cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
+    return step, 2, kernels, tokens, cpu, {**codec_config(w), "cached_tokens": T, "appended_per_step": 1}
 
 
 def setup_joint(torch, tq, W, w, dev):
@@ -358,7 +364,59 @@ def setup_joint(torch, tq, W, w, dev):
                      k_bits=w.k_bits, k_out=ko, v_out=vo)
 
     _, dec_b = row_bytes(w)
-    return step, 1, {"decode": (0, 1, w.rows * dec_b)}, (lambda i: w.kv_tokens), (lambda: sample), {}
+    cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
+    return step, 1, {"decode": (0, 1, w.rows * dec_b)}, (lambda i: w.kv_tokens), cpu, codec_config(w)
+
+
+def codec_config(w):
+    return {"workload": DESCRIPTION[w.name], "tokens": w.kv_tokens, "heads": w.heads, "head_dim": w.head_dim,
+            "v_bits": w.v_bits, "k_bits": w.k_bits, "k_signed": w.k_signed, "input_dtype": w.dtype}
+
+
+def setup_batch_merge(torch, tq, W, dev):
+    """Merge 32 caches into one left-padded batch per step."""
+    m = W.MERGE
+    lens = W.merge_lengths()
+    H, d, kb, vb = m["heads"], m["head_dim"], m["k_bits"], m["v_bits"]
+    caches = [W.random_planes(n, H, d, kb, vb, seed=m["seed"] * 1000 + i, device=dev) for i, n in enumerate(lens)]
+    width = max(lens)
+    dst = tq.empty_planes(len(lens) * width * H, d, kb, vb, dev)
+    tok_b = H * (d * (kb + vb) // 8 + 6 * (d // 32))  # plane bytes per token
+    nbytes = sum(lens) * tok_b + len(lens) * width * tok_b  # read the caches, write the batch
+    log(f"workload batch_merge: {len(lens)} caches, {sum(lens)} tokens, width {width}")
+    from kv_cache_quantization_tq_amd import _packed, TQConfig, TQPackedKV
+    import ctypes
+    import numpy as np
+    srcs = (TQPackedKV * len(lens))(*[_packed(c) for c in caches])
+    lens_a = np.asarray(lens, dtype=np.int64)
+    cfg = TQConfig(d, kb, vb, 0)
+    pk = _packed(dst)
+    stream = ctypes_stream(torch)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        st = tq.lib().tq_merge_rows(srcs, lens_a.ctypes.data, len(lens), width, H, ctypes.byref(cfg),
+                                    ctypes.byref(pk), None, stream)
+        if st:
+            raise tq.TQError(st, "tq_merge_rows")
+
+    def cpu():
+        import oracle.batching as OB
+        ns = 8  # the first 8 caches
+        host = [{n: (p.cpu().numpy().view(np.uint16) if p.dtype == torch.int16 else p.cpu().numpy())
+                 for n, p in c.items()} for c in caches[:ns]]
+        t0 = time.perf_counter()
+        OB.merge_rows(host, H)
+        t = time.perf_counter() - t0
+        ntok = sum(lens[:ns])
+        log(f"cpu oracle (merge of {ns} caches, {ntok} tokens): {t:.2f} s")
+        return {"value": ntok / t, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"merge of the first {ns} of the 32 caches ({ntok} tokens), one thread (numpy)"}
+
+    config = {"workload": DESCRIPTION["batch_merge"], "sequences": len(lens), "tokens": sum(lens), "width": width,
+              "heads": H, "head_dim": d, "v_bits": vb, "k_bits": kb}
+    return step, 1, {"merge": (0, 1, nbytes)}, (lambda i: sum(lens)), cpu, config
 
 
 def main():
@@ -388,16 +446,18 @@ def main():
         sys.exit(1)
     tq.lib()
     dev = torch.device("cuda:0")
-    w = W.WORKLOADS[args.workload]
-    steps = args.steps or (20 if args.workload in ("long_decode", "joint_large") else 50)
+    w = W.WORKLOADS.get(args.workload)
+    steps = args.steps or (20 if args.workload in ("long_decode", "joint_large", "batch_merge") else 50)
 
     if args.workload in ("prefill", "small_head"):
-        step, marks, kernels, tokens, host, extra = setup_encode_decode(torch, tq, W, w, dev, args.sets)
+        step, marks, kernels, tokens, cpu_fn, config = setup_encode_decode(torch, tq, W, w, dev, args.sets)
     elif args.workload == "long_decode":
-        step, marks, kernels, tokens, host, extra = setup_long_decode(torch, tq, W, w, dev,
-                                                                      args.warmup + steps)
+        step, marks, kernels, tokens, cpu_fn, config = setup_long_decode(torch, tq, W, w, dev,
+                                                                         args.warmup + steps)
+    elif args.workload == "joint_large":
+        step, marks, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
     else:
-        step, marks, kernels, tokens, host, extra = setup_joint(torch, tq, W, w, dev)
+        step, marks, kernels, tokens, cpu_fn, config = setup_batch_merge(torch, tq, W, dev)
     torch.cuda.synchronize()
 
     if args.copy_calibration_mib:
@@ -440,13 +500,7 @@ def main():
         f"device copy reference {copy_gbps:.0f} GB/s")
 
     dom = max(stats, key=lambda n: stats[n]["avg_us"])
-    cpu = None
-    if not args.no_cpu_baseline:
-        kn, vn = host()
-        if args.workload in ("prefill", "small_head"):
-            cpu = cpu_baseline(w, kn, vn, True, True, 1.0 / w.heads)
-        else:
-            cpu = cpu_baseline(w, kn, vn, False, True, 1.0 / w.heads)
+    cpu = None if args.no_cpu_baseline else cpu_fn()
 
     out = {
         "metric": METRIC[args.workload],
@@ -459,11 +513,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "u8" if args.workload == "batch_merge" else "f32",
         "data": "synthetic",
-        "config": {"workload": DESCRIPTION[args.workload], "tokens": w.kv_tokens, "heads": w.heads,
-                   "head_dim": w.head_dim, "v_bits": w.v_bits, "k_bits": w.k_bits,
-                   "k_signed": w.k_signed, "input_dtype": w.dtype, **extra},
+        "config": config,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": stats[dom]["GBps"], "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": stats[dom]["GBps"] / PEAK_HBM_GBPS,
                      "traffic": measured_traffic(args.workload, dom),

@@ -45,10 +45,25 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def source_digest() -> str:
-    """SHA-256 over every codec source and the public header."""
+# The sources each kind of kernel is built from (with include/tq.h); a
+# measurement taken on a kernel stays valid while these files are unchanged.
+BATCH_SOURCES = ("tq_batch.hip", "tq_host.h")
+
+
+def kernel_sources(kind: str = "all"):
+    files = sorted(glob.glob(os.path.join(CSRC, "*")))
+    if kind == "merge":
+        files = [f for f in files if os.path.basename(f) in BATCH_SOURCES]
+    elif kind in ("encode", "decode", "unrotate", "codec"):
+        files = [f for f in files if os.path.basename(f) != "tq_batch.hip"]
+    return files + [os.path.join(ROOT, "include", "tq.h")]
+
+
+def source_digest(kind: str = "all") -> str:
+    """SHA-256 over the sources of one kind of kernel (all sources by default)
+    and the public header."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "tq.h")]:
+    for p in kernel_sources(kind):
         h.update(os.path.basename(p).encode())
         with open(p, "rb") as f:
             h.update(f.read())

@@ -2,7 +2,7 @@
 
     python -m kv_cache_quantization_tq_amd.profiling trace <kernel_trace.csv> [--stats <kernel_stats.csv>]
     python -m kv_cache_quantization_tq_amd.profiling traffic <fetch.csv> <write.csv> \
-        --copy-mib 512 [--json out.json]
+        --copy-mib 512 [--json out.json] [--ops merge=N]
 
 ``trace`` prints per-kernel dispatch counts and average / median / min
 durations from a ``--kernel-trace`` CSV, and with ``--stats`` the codec
@@ -10,7 +10,9 @@ kernels' rows of rocprofv3's own ``--stats`` table. ``traffic`` turns the FETCH_
 WRITE_SIZE counters (KiB per dispatch) of two ``--pmc`` runs of
 ``bench.py --copy-calibration-mib N`` into HBM bytes per launch: each
 counter is scaled by the factor that maps the same counter, read on the
-plain device copy of N MiB in the same run, to its known N MiB.
+plain device copy of N MiB in the same run, to its known N MiB. Each
+kernel's entry records the SHA-256 of the sources it is built from, so a
+reader can tell whether the figures still describe the current kernel.
 """
 from __future__ import annotations
 
@@ -32,13 +34,15 @@ def kernel_kind(name: str) -> str:
         return "decode"
     if "unrotate_kernel" in name:
         return "unrotate"
+    if "segment_copy_kernel" in name:
+        return "merge"
     if "copyBuffer" in name:
         return "copy"
     return "other"
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(\w+_kernel<[^>]*>)", name)
+    m = re.search(r"(\w+_kernel(<[^>]*>)?)", name)
     return m.group(1) if m else name[:80]
 
 
@@ -52,14 +56,18 @@ def read_trace(path: str):
     return out
 
 
-def trace_summary(path: str) -> str:
+def trace_summary(path: str, ops: dict | None = None) -> str:
     rows = []
-    for name, d in read_trace(path).items():
-        if kernel_kind(name) in ("encode", "decode", "unrotate"):
+    tr = read_trace(path)
+    for name, d in tr.items():
+        if kernel_kind(name) in ("encode", "decode", "unrotate", "merge"):
             rows.append((name, len(d), sum(d) / len(d), statistics.median(d), min(d)))
     lines = [f"{'kernel':70s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} {'min_us':>8s}"]
     for name, n, avg, med, mn in sorted(rows):
         lines.append(f"{name[:70]:70s} {n:5d} {avg:8.2f} {med:8.2f} {mn:8.2f}")
+    for kind, n in (ops or {}).items():
+        tot = sum(sum(d) for name, d in tr.items() if kernel_kind(name) == kind)
+        lines.append(f"{kind}: {n} operations, {tot / n:.2f} us of kernel time per operation")
     return "\n".join(lines)
 
 
@@ -68,7 +76,7 @@ def stats_summary(path: str) -> str:
     with open(path) as f:
         for r in csv.DictReader(f):
             name = short_name(r["Name"])
-            if kernel_kind(name) in ("encode", "decode", "unrotate"):
+            if kernel_kind(name) in ("encode", "decode", "unrotate", "merge"):
                 lines.append(f"{name[:70]:70s} {int(r['Calls']):5d} {float(r['AverageNs']) * 1e-3:8.2f} "
                              f"{float(r['MinNs']) * 1e-3:8.2f} {float(r['MaxNs']) * 1e-3:8.2f}")
     return "\n".join(lines)
@@ -84,7 +92,7 @@ def read_counter(path: str, counter: str):
     return out
 
 
-def traffic(fetch_csv: str, write_csv: str, copy_mib: int) -> dict:
+def traffic(fetch_csv: str, write_csv: str, copy_mib: int, ops: dict | None = None) -> dict:
     fetch = read_counter(fetch_csv, "FETCH_SIZE")
     write = read_counter(write_csv, "WRITE_SIZE")
     copy_kib = copy_mib * 1024.0
@@ -97,13 +105,22 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int) -> dict:
     f_scale = copy_kib / copy_reading(fetch)
     w_scale = copy_kib / copy_reading(write)
     from kv_cache_quantization_tq_amd.build import source_digest
-    res = {"source_sha256": source_digest(),
-           "copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
-    for kind in ("encode", "decode"):
+    res = {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for kind in ("encode", "decode", "merge"):
         fv = [v for n, vs in fetch.items() if kernel_kind(n) == kind for v in vs]
         wv = [v for n, vs in write.items() if kernel_kind(n) == kind for v in vs]
-        if fv and wv:
+        if fv and wv and ops and kind in ops:
+            # one operation is several launches: total over the run / operations
+            n = ops[kind]
             res["kernels"][kind] = {
+                "source_sha256": source_digest(kind), "operations": n, "dispatches": len(fv),
+                "fetch_kib_raw": sum(fv) / n, "write_kib_raw": sum(wv) / n,
+                "fetch_bytes": int(sum(fv) / n * f_scale * 1024),
+                "write_bytes": int(sum(wv) / n * w_scale * 1024),
+            }
+        elif fv and wv:
+            res["kernels"][kind] = {
+                "source_sha256": source_digest(kind),
                 "fetch_kib_raw": statistics.median(fv), "write_kib_raw": statistics.median(wv),
                 "fetch_bytes": int(statistics.median(fv) * f_scale * 1024),
                 "write_bytes": int(statistics.median(wv) * w_scale * 1024),
@@ -117,19 +134,23 @@ def main(argv=None):
     t = sub.add_parser("trace")
     t.add_argument("csv")
     t.add_argument("--stats")
+    t.add_argument("--ops", action="append", default=[], help="KIND=N: also report kernel time per operation")
     c = sub.add_parser("traffic")
     c.add_argument("fetch_csv")
     c.add_argument("write_csv")
     c.add_argument("--copy-mib", type=int, required=True)
     c.add_argument("--json")
+    c.add_argument("--ops", action="append", default=[],
+                   help="KIND=N: that kind's launches form N operations; report bytes per operation")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace_summary(a.csv))
+        print(trace_summary(a.csv, {k: int(v) for k, v in (o.split("=") for o in a.ops)}))
         if a.stats:
             print()
             print(stats_summary(a.stats))
     else:
-        res = traffic(a.fetch_csv, a.write_csv, a.copy_mib)
+        ops = {k: int(v) for k, v in (o.split("=") for o in a.ops)}
+        res = traffic(a.fetch_csv, a.write_csv, a.copy_mib, ops)
         txt = json.dumps(res, indent=1)
         if a.json:
             with open(a.json, "w") as f:

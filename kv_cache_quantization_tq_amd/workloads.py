@@ -25,6 +25,12 @@ model K/V caches:
                   rows in K and V); values 8-bit (one byte per code), keys
                   4-bit; one pass decodes K and V together.
 
+* ``batch_merge`` 32 packed caches of 8 KV heads, head_dim 128, values
+                  4-bit / keys 4-bit, with lengths drawn uniformly in
+                  [4096, 32768] tokens (seed 5), merged into one left-padded
+                  batch (the token-axis batching operations move bytes, so
+                  the plane contents are seeded random bytes).
+
 Batches fold into the token axis: tensors are [batch * tokens, heads, d].
 Small tensors are drawn on the host with numpy; large ones on the target
 device with a seeded torch generator, in token chunks.
@@ -164,3 +170,30 @@ def to_oracle(t) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+# ---------------------------------------------------------------- batching
+
+MERGE = dict(sequences=32, heads=8, head_dim=128, k_bits=4, v_bits=4, min_len=4096, max_len=32768, seed=5)
+
+
+def merge_lengths(sequences=MERGE["sequences"], lo=MERGE["min_len"], hi=MERGE["max_len"], seed=MERGE["seed"]):
+    """Token counts of the caches merged by the batching workload."""
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(lo, hi + 1, sequences)]
+
+
+def random_planes(tokens: int, heads: int, head_dim: int, k_bits: int, v_bits: int, seed: int, device="cpu"):
+    """A plane dict (k_codes, k_scale, k_zero, v_codes, v_scale) of seeded
+    random bytes for `tokens` tokens; fp16 planes are int16 tensors."""
+    torch = _torch()
+    g = _gen(device, seed)
+    G = head_dim // 32
+    shapes = {"k_codes": (head_dim * k_bits // 8, torch.uint8), "k_scale": (G, torch.int16),
+              "k_zero": (G, torch.int16), "v_codes": (head_dim * v_bits // 8, torch.uint8),
+              "v_scale": (G, torch.int16)}
+    out = {}
+    for name, (width, dt) in shapes.items():
+        lo, hi = (0, 256) if dt == torch.uint8 else (-32768, 32768)
+        out[name] = torch.randint(lo, hi, (tokens * heads, width), generator=g, device=device, dtype=dt)
+    return out

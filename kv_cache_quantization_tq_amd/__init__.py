@@ -34,6 +34,7 @@ EXPORTS = (
     "tq_packed_dim", "tq_status_string", "tq_encode_kv", "tq_decode_kv", "tq_unrotate_values",
     "tq_lloyd_max_table", "tq_sign_vector", "tq_value_bin_host",
     "tq_merge_rows", "tq_extend_rows", "tq_extract_row", "tq_filter_rows",
+    "tq_lloyd_max_workspace_bytes", "tq_lloyd_max_fit",
 )
 
 
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
             "tq_filter_rows": (i32, [ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
                                      ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
+            "tq_lloyd_max_workspace_bytes": (i64, []),
+            "tq_lloyd_max_fit": (i32, [P, i64, i32, P, i32, P, P, P, i64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -334,3 +337,29 @@ def filter_rows(batch, b: int, width: int, keep, *, heads: int, head_dim: int, k
     if st:
         raise TQError(st, "tq_filter_rows")
     return dst
+
+
+# ------------------------------------------------------- Lloyd-Max fitting
+
+def lloyd_max_fit(samples, levels: int, init, iterations: int = 500, workspace=None, stream=None):
+    """Fit `levels` Lloyd-Max levels to `samples` (a float32 device tensor)
+    from the ascending initial centroids `init`. Returns (centroids,
+    boundaries) as float64 numpy arrays. Waits for the stream."""
+    import numpy as np
+    torch = _torch()
+    if samples.dtype != torch.float32 or not samples.is_contiguous():
+        raise ValueError("samples must be a contiguous float32 tensor")
+    init_a = np.ascontiguousarray(np.asarray(init, dtype=np.float64))
+    if init_a.size != levels:
+        raise ValueError("init must hold `levels` values")
+    nbytes = int(lib().tq_lloyd_max_workspace_bytes())
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=samples.device)
+    c = np.zeros(levels, np.float64)
+    b = np.zeros(max(levels - 1, 1), np.float64)
+    st = lib().tq_lloyd_max_fit(_ptr(samples), samples.numel(), levels, init_a.ctypes.data, iterations,
+                                c.ctypes.data, b.ctypes.data, _ptr(workspace), workspace.numel(),
+                                _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_lloyd_max_fit")
+    return c, b[: levels - 1]

@@ -201,3 +201,26 @@ def test_batching_argument_validation():
     assert L.tq_filter_rows(by(dst), 2, 5, keep, 2, 2, by(cfg), by(dst), None) == tq.TQ_E_SHAPE  # keep[1] >= b
     assert L.tq_filter_rows(by(dst), 2, 5, None, 2, 2, by(cfg), by(dst), None) == tq.TQ_E_NULL
     assert L.tq_filter_rows(by(dst), 2, 5, None, 0, 2, by(cfg), by(dst), None) == tq.TQ_OK
+
+
+def test_lloyd_fit_argument_validation():
+    import numpy as np
+    L = tq.lib()
+    ws = int(L.tq_lloyd_max_workspace_bytes())
+    assert ws > 256 * 8 * 4
+    init = np.linspace(-1, 1, 4)
+    c = np.zeros(4)
+    b = np.zeros(3)
+    ip, cp, bp = init.ctypes.data, c.ctypes.data, b.ctypes.data
+    assert L.tq_lloyd_max_fit(FAKE, 10, 1, ip, 5, cp, bp, FAKE, ws, None) == tq.TQ_E_BITS
+    assert L.tq_lloyd_max_fit(FAKE, 10, 257, ip, 5, cp, bp, FAKE, ws, None) == tq.TQ_E_BITS
+    assert L.tq_lloyd_max_fit(FAKE, 0, 4, ip, 5, cp, bp, FAKE, ws, None) == tq.TQ_E_SHAPE
+    assert L.tq_lloyd_max_fit(FAKE, 10, 4, ip, -1, cp, bp, FAKE, ws, None) == tq.TQ_E_SHAPE
+    assert L.tq_lloyd_max_fit(None, 10, 4, ip, 5, cp, bp, FAKE, ws, None) == tq.TQ_E_NULL
+    assert L.tq_lloyd_max_fit(FAKE, 10, 4, None, 5, cp, bp, FAKE, ws, None) == tq.TQ_E_NULL
+    assert L.tq_lloyd_max_fit(FAKE, 10, 4, ip, 5, cp, bp, None, ws, None) == tq.TQ_E_NULL
+    assert L.tq_lloyd_max_fit(FAKE, 10, 4, ip, 5, cp, bp, FAKE, ws - 1, None) == tq.TQ_E_SHAPE
+    assert L.tq_lloyd_max_fit(FAKE + 2, 10, 4, ip, 5, cp, bp, FAKE, ws, None) == tq.TQ_E_ALIGN
+    assert L.tq_lloyd_max_fit(FAKE, 10, 4, ip, 5, cp, bp, FAKE + 4, ws, None) == tq.TQ_E_ALIGN
+    bad = np.array([-1.0, 0.0, 0.0, 1.0])   # not strictly ascending
+    assert L.tq_lloyd_max_fit(FAKE, 10, 4, bad.ctypes.data, 5, cp, bp, FAKE, ws, None) == tq.TQ_E_SHAPE

@@ -19,7 +19,9 @@ Lloyd-Max, keys 4-bit affine. What one step is:
                        heads, head_dim 512) to bf16;
 * batch_merge          merge 32 packed caches of 4096..32768 tokens into one
                        left-padded batch (the token-axis batching
-                       operation; KV tokens = tokens merged).
+                       operation; KV tokens = tokens merged);
+* lloyd_fit            one 500-iteration Lloyd-Max fit of 16 levels to 2^24
+                       samples (value = sample-iterations per second).
 
 Inputs are resident in HBM before timing starts. Prints one JSON line:
 value = KV tokens per second (one KV token = one position with K and V of
@@ -59,6 +61,8 @@ DESCRIPTION = {
                    "rows zeroed; values 8-bit (unpacked bytes), keys 4-bit; one joint K/V decode to bf16",
     "batch_merge": "batch_merge: 32 packed caches (8 KV heads, head_dim 128, V4/K4 planes of seeded random "
                    "bytes) of 4096..32768 tokens merged into one left-padded batch",
+    "lloyd_fit": "lloyd_fit: 4-bit (16-level) Lloyd-Max table fitted to 2^24 N(0,1) float32 samples, 500 "
+                 "iterations from the printed table",
 }
 
 METRIC = {
@@ -69,6 +73,7 @@ METRIC = {
     "joint_large": "KV tokens/sec joint K/V decode (d=512, V8/K4) and achieved HBM GB/s vs peak",
     "batch_merge": "KV tokens/sec merged into a left-padded batch (d=128, V4/K4 planes) and achieved HBM GB/s "
                    "vs peak",
+    "lloyd_fit": "Lloyd-Max fit sample-iterations/sec (16 levels, 2^24 samples) and achieved HBM GB/s vs peak",
 }
 
 
@@ -419,6 +424,38 @@ def setup_batch_merge(torch, tq, W, dev):
     return step, 1, {"merge": (0, 1, nbytes)}, (lambda i: sum(lens)), cpu, config
 
 
+def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
+    """One full fit per step; an iteration reads every sample once."""
+    n, levels = 1 << 24, 16
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    x = torch.randn(n, generator=g, device=dev, dtype=torch.float32)
+    init = tq.lloyd_max_table(4)[0].astype("float64")
+    ws = torch.empty(int(tq.lib().tq_lloyd_max_workspace_bytes()), dtype=torch.uint8, device=dev)
+    log(f"workload lloyd_fit: {n} samples, {levels} levels, {iterations} iterations per step")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        tq.lloyd_max_fit(x, levels, init, iterations, workspace=ws)
+
+    def cpu():
+        import numpy as np
+        from oracle import lloyd as OL
+        ns, it = 1 << 20, 5
+        xs = x[:ns].cpu().numpy()
+        t0 = time.perf_counter()
+        OL.fit_samples(xs, init, it)
+        t = time.perf_counter() - t0
+        log(f"cpu oracle (fit of {ns} samples, {it} iterations): {t:.2f} s")
+        return {"value": ns * it / t, "unit": "sample-iterations/s", "cores": 1, "kind": "oracle",
+                "sample": f"{it} iterations on the first {ns} samples, one thread (numpy)"}
+
+    config = {"workload": DESCRIPTION["lloyd_fit"], "samples": n, "levels": levels, "iterations": iterations}
+    # per step: `iterations` passes over the samples (4 bytes each)
+    return step, 1, {"fit": (0, 1, 4 * n * iterations)}, (lambda i: n * iterations), cpu, config
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -447,7 +484,7 @@ def main():
     tq.lib()
     dev = torch.device("cuda:0")
     w = W.WORKLOADS.get(args.workload)
-    steps = args.steps or (20 if args.workload in ("long_decode", "joint_large", "batch_merge") else 50)
+    steps = args.steps or {"long_decode": 20, "joint_large": 20, "batch_merge": 20, "lloyd_fit": 3}.get(args.workload, 50)
 
     if args.workload in ("prefill", "small_head"):
         step, marks, kernels, tokens, cpu_fn, config = setup_encode_decode(torch, tq, W, w, dev, args.sets)
@@ -456,8 +493,10 @@ def main():
                                                                          args.warmup + steps)
     elif args.workload == "joint_large":
         step, marks, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
-    else:
+    elif args.workload == "batch_merge":
         step, marks, kernels, tokens, cpu_fn, config = setup_batch_merge(torch, tq, W, dev)
+    else:
+        step, marks, kernels, tokens, cpu_fn, config = setup_lloyd_fit(torch, tq, W, dev)
     torch.cuda.synchronize()
 
     if args.copy_calibration_mib:
@@ -505,7 +544,7 @@ def main():
     out = {
         "metric": METRIC[args.workload],
         "value": kv_tokens / (steps * ms_per_step * 1e-3),
-        "unit": "KV tokens/s",
+        "unit": "sample-iterations/s" if args.workload == "lloyd_fit" else "KV tokens/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
@@ -513,7 +552,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8" if args.workload == "batch_merge" else "f32",
+        "dtype": {"batch_merge": "u8", "lloyd_fit": "f64"}.get(args.workload, "f32"),
         "data": "synthetic",
         "config": config,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": stats[dom]["GBps"], "peak": PEAK_HBM_GBPS,

@@ -48,14 +48,17 @@ def sources():
 # The sources each kind of kernel is built from (with include/tq.h); a
 # measurement taken on a kernel stays valid while these files are unchanged.
 BATCH_SOURCES = ("tq_batch.hip", "tq_host.h")
+FIT_SOURCES = ("tq_fit.hip",)
 
 
 def kernel_sources(kind: str = "all"):
     files = sorted(glob.glob(os.path.join(CSRC, "*")))
     if kind == "merge":
         files = [f for f in files if os.path.basename(f) in BATCH_SOURCES]
+    elif kind == "fit":
+        files = [f for f in files if os.path.basename(f) in FIT_SOURCES]
     elif kind in ("encode", "decode", "unrotate", "codec"):
-        files = [f for f in files if os.path.basename(f) != "tq_batch.hip"]
+        files = [f for f in files if os.path.basename(f) not in ("tq_batch.hip",) + FIT_SOURCES]
     return files + [os.path.join(ROOT, "include", "tq.h")]
 
 

@@ -9,7 +9,9 @@
 //                                          the lower level)
 //   centroids   c_k = mean of the samples with k(x) = k    (a level with no
 //                                          sample keeps its centroid)
-// This file runs the iterations on the device with no host round trip.
+// This file runs the iterations on the device with no host round trip (per
+// iteration an assignment launch writing per-block partial sums and an
+// update launch with one block per level).
 //
 // Determinism: each sample enters the per-level sums as the exact integer
 // rint(x * 2^s), with s chosen from the sample count and the largest
@@ -28,27 +30,46 @@ namespace {
 
 constexpr int kMaxLevels = 256;
 constexpr int kFitThreads = 256;
-constexpr int kFitWaves = kFitThreads / 64;
+constexpr int kFitBlocks = 1024; // most blocks of a pass (per-block partials below)
 
-// Device workspace (caller-owned).
+// Device workspace (caller-owned). Each pass writes one partial result per
+// block (no contended atomics: a handful of addresses hit by every block
+// of every XCD would serialise), reduced by the next step.
 struct FitWork {
     double cent[kMaxLevels];
-    double bnd[kMaxLevels];          // L - 1 boundaries, then +inf
-    unsigned long long sum[kMaxLevels]; // two's complement int64
-    unsigned long long cnt[kMaxLevels];
-    unsigned int absmax_bits;        // largest |x| as float bits (NaN bits if any sample is NaN)
-    int shift;                       // s, or -1 when the samples cannot be fitted
+    unsigned long long part_sum[kFitBlocks][kMaxLevels]; // two's complement int64
+    unsigned int part_cnt[kFitBlocks][kMaxLevels];
+    unsigned int part_max[kFitBlocks];                   // largest |x| bits per block
+    int shift;                                           // s, or -1 when the samples cannot be fitted
 };
 
-// largest |x| (as the bit pattern of a non-negative float, whose integer
-// order is the float order; NaN patterns order above +inf)
+// largest |x| of a block's samples as the bit pattern of a non-negative
+// float (its integer order is the float order; NaN patterns order above
+// +inf)
 __global__ void __launch_bounds__(kFitThreads) fit_absmax_kernel(const float *x, int64_t n, FitWork *w)
 {
     unsigned int m = 0;
-    for (int64_t i = (int64_t)blockIdx.x * kFitThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kFitThreads)
-        m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
+    const int64_t tid = (int64_t)blockIdx.x * kFitThreads + threadIdx.x, nt = (int64_t)gridDim.x * kFitThreads;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        // whole 16-byte vectors, then the last n % 4 samples
+        const float4 *x4 = reinterpret_cast<const float4 *>(x);
+        for (int64_t v = tid; v < n / 4; v += nt) {
+            const float4 a = x4[v];
+            m = max(max(m, __float_as_uint(a.x) & 0x7fffffffu), __float_as_uint(a.y) & 0x7fffffffu);
+            m = max(max(m, __float_as_uint(a.z) & 0x7fffffffu), __float_as_uint(a.w) & 0x7fffffffu);
+        }
+        if (tid < n % 4) m = max(m, __float_as_uint(x[n / 4 * 4 + tid]) & 0x7fffffffu);
+    } else {
+        for (int64_t i = tid; i < n; i += nt) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
+    }
     for (int o = 32; o > 0; o >>= 1) m = max(m, (unsigned int)__shfl_xor((int)m, o));
-    if ((threadIdx.x & 63) == 0) atomicMax(&w->absmax_bits, m);
+    __shared__ unsigned int wm[kFitThreads / 64];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x / 64] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < kFitThreads / 64; ++i) m = max(m, wm[i]);
+        w->part_max[blockIdx.x] = m;
+    }
 }
 
 // s = min(40, 62 - bitlen(n) - e) with |x| < 2^e for every sample: every
@@ -64,79 +85,143 @@ __device__ int fit_shift(unsigned int absmax_bits, int64_t n)
     return s > 40 ? 40 : s;
 }
 
-__device__ void fit_boundaries(FitWork *w, int levels)
+// one block: the largest magnitude over the absmax blocks, then the shift
+__global__ void __launch_bounds__(kFitThreads) fit_init_kernel(FitWork *w, int blocks, int64_t n)
 {
+    __shared__ unsigned int red[kFitThreads];
+    unsigned int m = 0;
+    for (int b = threadIdx.x; b < blocks; b += kFitThreads) m = max(m, w->part_max[b]);
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int h = kFitThreads / 2; h > 0; h >>= 1) {
+        if (threadIdx.x < h) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + h]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) w->shift = fit_shift(red[0], n);
+}
+
+// Assignment and per-level integer sums of one pass. The block computes the
+// boundaries from the current centroids, keeps R replicas of the L-level
+// histogram in LDS (R = the largest power of two <= 64 with R * L <=
+// kHistEntries), lane l of every wavefront adding into replica l % R so
+// that lanes of one wavefront rarely contend for an address, folds the
+// replicas pairwise and writes the block's totals as its partial. The
+// search compares the float32 sample with each boundary rounded down to
+// float32, which decides b < x exactly (no float32 lies strictly between a
+// binary64 value and its round-down).
+constexpr int kHistEntries = 1024;
+
+__host__ __device__ inline int fit_replicas(int levels)
+{
+    int r = 64;
+    while (r > 1 && r * levels > kHistEntries) r >>= 1;
+    return r;
+}
+
+__global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x, int64_t n, int levels, FitWork *w)
+{
+    __shared__ float bnd[kMaxLevels];
+    __shared__ unsigned long long hsum[kHistEntries];
+    __shared__ unsigned int hcnt[kHistEntries];
+    const int s = w->shift;
+    if (s < 0) return;
+    const int R = fit_replicas(levels);
     for (int j = threadIdx.x; j < kMaxLevels; j += kFitThreads)
-        w->bnd[j] = j < levels - 1 ? (w->cent[j] + w->cent[j + 1]) * 0.5 : (double)INFINITY;
-}
-
-// one block: the shift, the first boundaries, cleared accumulators
-__global__ void __launch_bounds__(kFitThreads) fit_init_kernel(FitWork *w, int levels, int64_t n)
-{
-    if (threadIdx.x == 0) w->shift = fit_shift(w->absmax_bits, n);
-    for (int j = threadIdx.x; j < kMaxLevels; j += kFitThreads) {
-        w->sum[j] = 0;
-        w->cnt[j] = 0;
-    }
-    fit_boundaries(w, levels);
-}
-
-// assignment and per-level integer sums; per-wavefront LDS histograms,
-// merged into the workspace with integer atomics
-__global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x, int64_t n, FitWork *w)
-{
-    __shared__ double bnd[kMaxLevels];
-    __shared__ unsigned long long hsum[kFitWaves][kMaxLevels];
-    __shared__ unsigned int hcnt[kFitWaves][kMaxLevels];
-    const int s = w->shift;
-    if (s < 0) return;
-    for (int j = threadIdx.x; j < kMaxLevels; j += kFitThreads) {
-        bnd[j] = w->bnd[j];
-        for (int v = 0; v < kFitWaves; ++v) {
-            hsum[v][j] = 0;
-            hcnt[v][j] = 0;
-        }
+        bnd[j] = j < levels - 1 ? __double2float_rd((w->cent[j] + w->cent[j + 1]) * 0.5) : INFINITY;
+    for (int j = threadIdx.x; j < levels * R; j += kFitThreads) {
+        hsum[j] = 0;
+        hcnt[j] = 0;
     }
     __syncthreads();
-    const int wave = threadIdx.x / 64;
-    for (int64_t i = (int64_t)blockIdx.x * kFitThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kFitThreads) {
-        const double xd = (double)x[i];
-        // k = #{ j : bnd[j] < x } over 255 sorted entries padded with +inf
-        int k = 0;
+    // binary search over the sorted boundaries (padded with +inf): the
+    // first step is the largest power of two below `levels`
+    int top = 1;
+    while (top * 2 < levels) top *= 2;
+    const int rep = (threadIdx.x & 63) % R;
+    // four samples at a time (one 16-byte vector per thread and step when
+    // the samples are 16-byte aligned), so that their searches overlap
+    auto add4 = [&](const float (&v)[4], int valid) {
+        int k[4] = {0, 0, 0, 0};
+        for (int step = top; step > 0; step >>= 1) {
 #pragma unroll
-        for (int step = 128; step > 0; step >>= 1)
-            if (bnd[k + step - 1] < xd) k += step;
-        const long long q = (long long)rint(ldexp(xd, s));
-        atomicAdd(&hsum[wave][k], (unsigned long long)q);
-        atomicAdd(&hcnt[wave][k], 1u);
+            for (int u = 0; u < 4; ++u)
+                if (bnd[k[u] + step - 1] < v[u]) k[u] += step;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (u < valid) {
+                const long long q = (long long)rint(ldexp((double)v[u], s));
+                atomicAdd(&hsum[k[u] * R + rep], (unsigned long long)q);
+                atomicAdd(&hcnt[k[u] * R + rep], 1u);
+            }
+        }
+    };
+    const int64_t tid = (int64_t)blockIdx.x * kFitThreads + threadIdx.x, nt = (int64_t)gridDim.x * kFitThreads;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(x);
+        for (int64_t vi = tid; vi < n / 4; vi += nt) {
+            const float4 a = x4[vi];
+            const float v[4] = {a.x, a.y, a.z, a.w};
+            add4(v, 4);
+        }
+        if (tid == 0 && n % 4 != 0) {
+            float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int u = 0; u < (int)(n % 4); ++u) v[u] = x[n / 4 * 4 + u];
+            add4(v, (int)(n % 4));
+        }
+    } else {
+        for (int64_t i0 = tid; i0 < n; i0 += 4 * nt) {
+            float v[4];
+            int valid = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t i = i0 + u * nt;
+                v[u] = i < n ? x[i] : 0.0f;
+                valid += i < n ? 1 : 0;
+            }
+            add4(v, valid);
+        }
     }
     __syncthreads();
-    for (int j = threadIdx.x; j < kMaxLevels; j += kFitThreads) {
-        unsigned long long sm = 0, c = 0;
-        for (int v = 0; v < kFitWaves; ++v) {
-            sm += hsum[v][j];
-            c += hcnt[v][j];
+    for (int half = R / 2; half > 0; half >>= 1) {
+        for (int j = threadIdx.x; j < levels * half; j += kFitThreads) {
+            const int kk = j / half, r = j % half;
+            hsum[kk * R + r] += hsum[kk * R + r + half];
+            hcnt[kk * R + r] += hcnt[kk * R + r + half];
         }
-        if (c != 0) {
-            atomicAdd(&w->sum[j], sm);
-            atomicAdd(&w->cnt[j], c);
-        }
+        __syncthreads();
+    }
+    for (int kk = threadIdx.x; kk < levels; kk += kFitThreads) {
+        w->part_sum[blockIdx.x][kk] = hsum[kk * R];
+        w->part_cnt[blockIdx.x][kk] = hcnt[kk * R];
     }
 }
 
-// one block: new centroids from the sums, new boundaries, cleared sums
-__global__ void __launch_bounds__(kFitThreads) fit_update_kernel(FitWork *w, int levels)
+// one block per level: the level's total over the pass's block partials,
+// then its new centroid (a level with no sample keeps its value)
+__global__ void __launch_bounds__(kFitThreads) fit_update_kernel(FitWork *w, int blocks)
 {
+    __shared__ unsigned long long rs[kFitThreads];
+    __shared__ unsigned long long rc[kFitThreads];
     const int s = w->shift;
     if (s < 0) return;
-    for (int j = threadIdx.x; j < levels; j += kFitThreads) {
-        const unsigned long long c = w->cnt[j];
-        if (c != 0) w->cent[j] = ldexp((double)(long long)w->sum[j], -s) / (double)c;
-        w->sum[j] = 0;
-        w->cnt[j] = 0;
+    const int k = blockIdx.x;
+    unsigned long long sm = 0, c = 0;
+    for (int b = threadIdx.x; b < blocks; b += kFitThreads) {
+        sm += w->part_sum[b][k];
+        c += w->part_cnt[b][k];
     }
+    rs[threadIdx.x] = sm;
+    rc[threadIdx.x] = c;
     __syncthreads();
-    fit_boundaries(w, levels);
+    for (int h = kFitThreads / 2; h > 0; h >>= 1) {
+        if (threadIdx.x < h) {
+            rs[threadIdx.x] += rs[threadIdx.x + h];
+            rc[threadIdx.x] += rc[threadIdx.x + h];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0 && rc[0] != 0) w->cent[k] = ldexp((double)(long long)rs[0], -s) / (double)rc[0];
 }
 
 int32_t hip_ok(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_HIP; }
@@ -162,33 +247,29 @@ int32_t tq_lloyd_max_fit(const float *samples, int64_t n, int32_t levels, const 
     hipStream_t st = (hipStream_t)stream;
     FitWork *w = static_cast<FitWork *>(workspace);
     int32_t r = TQ_OK;
-    const unsigned int zero = 0;
     if ((r = hip_ok(hipMemcpyAsync(w->cent, init, sizeof(double) * levels, hipMemcpyHostToDevice, st))) != TQ_OK)
-        return r;
-    if ((r = hip_ok(hipMemcpyAsync(&w->absmax_bits, &zero, sizeof(zero), hipMemcpyHostToDevice, st))) != TQ_OK)
         return r;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                  hipSuccess || cus <= 0)
         cus = 256;
-    const int64_t want = (n + kFitThreads - 1) / kFitThreads;
-    const unsigned int grid = (unsigned int)(want < 4LL * cus ? want : 4LL * cus);
+    const int64_t want = (n / 4 + kFitThreads) / kFitThreads;
+    const int64_t cap = 4LL * cus < kFitBlocks ? 4LL * cus : kFitBlocks;
+    const int grid = (int)(want < cap ? want : cap);
     hipLaunchKernelGGL(fit_absmax_kernel, dim3(grid), dim3(kFitThreads), 0, st, samples, n, w);
-    hipLaunchKernelGGL(fit_init_kernel, dim3(1), dim3(kFitThreads), 0, st, w, (int)levels, n);
+    hipLaunchKernelGGL(fit_init_kernel, dim3(1), dim3(kFitThreads), 0, st, w, grid, n);
     for (int32_t it = 0; it < iterations; ++it) {
-        hipLaunchKernelGGL(fit_assign_kernel, dim3(grid), dim3(kFitThreads), 0, st, samples, n, w);
-        hipLaunchKernelGGL(fit_update_kernel, dim3(1), dim3(kFitThreads), 0, st, w, (int)levels);
+        hipLaunchKernelGGL(fit_assign_kernel, dim3(grid), dim3(kFitThreads), 0, st, samples, n, (int)levels, w);
+        hipLaunchKernelGGL(fit_update_kernel, dim3(levels), dim3(kFitThreads), 0, st, w, grid);
     }
     if ((r = hip_ok(hipGetLastError())) != TQ_OK) return r;
     int shift = 0;
     if ((r = hip_ok(hipMemcpyAsync(centroids, w->cent, sizeof(double) * levels, hipMemcpyDeviceToHost, st))) != TQ_OK)
         return r;
-    if (boundaries != nullptr &&
-        (r = hip_ok(hipMemcpyAsync(boundaries, w->bnd, sizeof(double) * (levels - 1), hipMemcpyDeviceToHost, st))) !=
-            TQ_OK)
-        return r;
     if ((r = hip_ok(hipMemcpyAsync(&shift, &w->shift, sizeof(int), hipMemcpyDeviceToHost, st))) != TQ_OK) return r;
     if ((r = hip_ok(hipStreamSynchronize(st))) != TQ_OK) return r;
+    if (boundaries != nullptr)
+        for (int j = 0; j < levels - 1; ++j) boundaries[j] = (centroids[j] + centroids[j + 1]) * 0.5;
     return shift < 0 ? TQ_E_SHAPE : TQ_OK;
 }
 

@@ -36,6 +36,8 @@ def kernel_kind(name: str) -> str:
         return "unrotate"
     if "segment_copy_kernel" in name:
         return "merge"
+    if "fit_" in name and "_kernel" in name:
+        return "fit"
     if "copyBuffer" in name:
         return "copy"
     return "other"
@@ -60,7 +62,7 @@ def trace_summary(path: str, ops: dict | None = None) -> str:
     rows = []
     tr = read_trace(path)
     for name, d in tr.items():
-        if kernel_kind(name) in ("encode", "decode", "unrotate", "merge"):
+        if kernel_kind(name) in ("encode", "decode", "unrotate", "merge", "fit"):
             rows.append((name, len(d), sum(d) / len(d), statistics.median(d), min(d)))
     lines = [f"{'kernel':70s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} {'min_us':>8s}"]
     for name, n, avg, med, mn in sorted(rows):
@@ -76,7 +78,7 @@ def stats_summary(path: str) -> str:
     with open(path) as f:
         for r in csv.DictReader(f):
             name = short_name(r["Name"])
-            if kernel_kind(name) in ("encode", "decode", "unrotate", "merge"):
+            if kernel_kind(name) in ("encode", "decode", "unrotate", "merge", "fit"):
                 lines.append(f"{name[:70]:70s} {int(r['Calls']):5d} {float(r['AverageNs']) * 1e-3:8.2f} "
                              f"{float(r['MinNs']) * 1e-3:8.2f} {float(r['MaxNs']) * 1e-3:8.2f}")
     return "\n".join(lines)
@@ -106,7 +108,7 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, ops: dict | None = No
     w_scale = copy_kib / copy_reading(write)
     from kv_cache_quantization_tq_amd.build import source_digest
     res = {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
-    for kind in ("encode", "decode", "merge"):
+    for kind in ("encode", "decode", "merge", "fit"):
         fv = [v for n, vs in fetch.items() if kernel_kind(n) == kind for v in vs]
         wv = [v for n, vs in write.items() if kernel_kind(n) == kind for v in vs]
         if fv and wv and ops and kind in ops:

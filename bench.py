@@ -21,7 +21,10 @@ Lloyd-Max, keys 4-bit affine. What one step is:
                        left-padded batch (the token-axis batching
                        operation; KV tokens = tokens merged);
 * lloyd_fit            one 500-iteration Lloyd-Max fit of 16 levels to 2^24
-                       samples (value = sample-iterations per second).
+                       samples (value = sample-iterations per second);
+* attn_decode          one query token per head attending over the
+                       long_decode cache, decoding inside the kernel (KV
+                       tokens = cached tokens attended).
 
 Inputs are resident in HBM before timing starts. Prints one JSON line:
 value = KV tokens per second (one KV token = one position with K and V of
@@ -63,6 +66,8 @@ DESCRIPTION = {
                    "bytes) of 4096..32768 tokens merged into one left-padded batch",
     "lloyd_fit": "lloyd_fit: 4-bit (16-level) Lloyd-Max table fitted to 2^24 N(0,1) float32 samples, 500 "
                  "iterations from the printed table",
+    "attn_decode": "attn_decode: one query token (32 heads, bf16) attending over the long_decode cache (131072 "
+                   "tokens x 8 KV heads, head_dim 256, V5/K4 packed), decoded inside the attention kernel",
 }
 
 METRIC = {
@@ -74,6 +79,8 @@ METRIC = {
     "batch_merge": "KV tokens/sec merged into a left-padded batch (d=128, V4/K4 planes) and achieved HBM GB/s "
                    "vs peak",
     "lloyd_fit": "Lloyd-Max fit sample-iterations/sec (16 levels, 2^24 samples) and achieved HBM GB/s vs peak",
+    "attn_decode": "KV tokens/sec attended per decode step over the packed cache (d=256, V5/K4, 32 query heads) "
+                   "and achieved HBM GB/s vs peak",
 }
 
 
@@ -456,6 +463,53 @@ def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
     return step, 1, {"fit": (0, 1, 4 * n * iterations)}, (lambda i: n * iterations), cpu, config
 
 
+def setup_attn_decode(torch, tq, W, dev):
+    """The long_decode cache, attended by one bf16 query token of 32 heads."""
+    w = W.WORKLOADS["long_decode"]
+    T, H, d, hq = w.tokens, w.heads, w.head_dim, 32
+    k, v = W.make_kv(w, dev)
+    planes = tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits)
+    torch.cuda.synchronize()
+    ns = 8192  # tokens of the oracle sample
+    sample = (W.to_oracle(k[:ns]), W.to_oracle(v[:ns]))
+    del k, v
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    q = torch.randn((1, hq, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((1, hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(int(tq.lib().tq_attention_workspace_bytes(1, hq, d, T)), dtype=torch.uint8, device=dev)
+    row_b = d * (w.k_bits + w.v_bits) // 8 + 6 * (d // 32)
+    nbytes = T * H * row_b + q.numel() * 2 + out.numel() * 4
+    log(f"workload attn_decode: {T} tokens x {H} KV heads, {hq} query heads, {T * H * row_b / 1e6:.1f} MB of cache")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        tq.attention_decode(q, planes, batch=1, width=T, kv_heads=H, head_dim=d, k_bits=w.k_bits,
+                            v_bits=w.v_bits, out=out, workspace=ws)
+
+    def cpu():
+        import numpy as np
+        import oracle as O
+        from oracle import attention as OA
+        kn, vn = sample
+        rows = ns * H
+        planes_h = O.encode_kv(kn.reshape(rows, d), vn.reshape(rows, d), head_dim=d, k_bits=w.k_bits,
+                               v_bits=w.v_bits)
+        qh = q.float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        kd, vr = OA.decoded_cache(planes_h, rows, d, w.k_bits, w.v_bits)
+        OA.attention_decode(qh, kd, vr, 1, ns, None, H, 1.0 / np.sqrt(d))
+        t = time.perf_counter() - t0
+        log(f"cpu oracle (decode + attention over {ns} tokens): {t:.2f} s")
+        return {"value": ns / t, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"decode + attention over the first {ns} tokens of the cache, one thread"}
+
+    config = {"workload": DESCRIPTION["attn_decode"], "tokens": T, "kv_heads": H, "q_heads": hq, "head_dim": d,
+              "v_bits": w.v_bits, "k_bits": w.k_bits, "q_dtype": "bf16"}
+    return step, 1, {"attention": (0, 1, nbytes)}, (lambda i: T), cpu, config
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -484,7 +538,8 @@ def main():
     tq.lib()
     dev = torch.device("cuda:0")
     w = W.WORKLOADS.get(args.workload)
-    steps = args.steps or {"long_decode": 20, "joint_large": 20, "batch_merge": 20, "lloyd_fit": 3}.get(args.workload, 50)
+    steps = args.steps or {"long_decode": 20, "joint_large": 20, "batch_merge": 20, "lloyd_fit": 3,
+                           "attn_decode": 50}.get(args.workload, 50)
 
     if args.workload in ("prefill", "small_head"):
         step, marks, kernels, tokens, cpu_fn, config = setup_encode_decode(torch, tq, W, w, dev, args.sets)
@@ -495,8 +550,10 @@ def main():
         step, marks, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
     elif args.workload == "batch_merge":
         step, marks, kernels, tokens, cpu_fn, config = setup_batch_merge(torch, tq, W, dev)
-    else:
+    elif args.workload == "lloyd_fit":
         step, marks, kernels, tokens, cpu_fn, config = setup_lloyd_fit(torch, tq, W, dev)
+    else:
+        step, marks, kernels, tokens, cpu_fn, config = setup_attn_decode(torch, tq, W, dev)
     torch.cuda.synchronize()
 
     if args.copy_calibration_mib:

@@ -199,6 +199,38 @@ int32_t tq_filter_rows(const tq_packed_kv *batch, int32_t b, int64_t width, cons
                        int32_t heads, const tq_config *cfg, const tq_packed_kv *dst, void *stream);
 
 /* ---------------------------------------------------------------------
+ * Attention of one query token per sequence over a packed cache (page
+ * "@mlx-bun/inference 0.0.0-stage -> 1.0.0", ops.ts decodeValuesRotated and
+ * unrotateValues: attention is linear in V, so it may run on values still
+ * in the rotated domain and un-rotate its output once per query row).
+ * Keys are decoded as decodeKeys does (bf16), values as
+ * decodeValuesRotated does (bf16); both inside the kernel, so the cache is
+ * read packed. With valid tokens t of sequence b and query head h reading
+ * KV head h / (q_heads / kv_heads):
+ *   s_t = scale * <q[b,h], K_t>,  p = softmax(s),  o_rot = sum_t p_t Vrot_t,
+ *   out[b,h] = unrotate(o_rot)   (normalised transform, then sign vector)
+ * in binary32 after decoding. A sequence with no valid token gives zeros.
+ * --------------------------------------------------------------------- */
+
+/* Bytes of device workspace tq_attention_decode needs (host only; <0 on
+ * invalid arguments). */
+int64_t tq_attention_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim, int64_t width);
+
+/* q: [batch, q_heads, head_dim] of q_dtype (16-byte aligned). cache: a
+ * batch of `batch` sequences of width `width` in the layout of the batching
+ * operations above (all five planes, alignment as for tq_decode_kv);
+ * left_pad: device int32 [batch] (tokens [left_pad[b], width) of sequence
+ * b are attended) or NULL for none. q_heads / kv_heads must be 1, 2, 4 or
+ * 8. out: [batch, q_heads, head_dim] of out_dtype (16-byte aligned).
+ * workspace: caller-owned device memory of tq_attention_workspace_bytes()
+ * (16-byte aligned; may be NULL when width is 0); calls sharing a workspace
+ * must not overlap. Two launches on `stream`. */
+int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *cache, int32_t batch, int64_t width,
+                            const int32_t *left_pad, int32_t kv_heads, int32_t q_heads, const tq_config *cfg,
+                            float scale, void *out, int32_t out_dtype, void *workspace, int64_t workspace_bytes,
+                            void *stream);
+
+/* ---------------------------------------------------------------------
  * Lloyd-Max table fitting (page "mlx-bun 0.0.9 -> 0.0.11",
  * src/mlx/turboquant-tables.ts, header of LLOYD_MAX: the tables are an
  * iterative Lloyd-Max fit to unit-normal samples, 500 iterations).

@@ -35,6 +35,7 @@ EXPORTS = (
     "tq_lloyd_max_table", "tq_sign_vector", "tq_value_bin_host",
     "tq_merge_rows", "tq_extend_rows", "tq_extract_row", "tq_filter_rows",
     "tq_lloyd_max_workspace_bytes", "tq_lloyd_max_fit",
+    "tq_attention_workspace_bytes", "tq_attention_decode",
 )
 
 
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
             "tq_filter_rows": (i32, [ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
                                      ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
             "tq_lloyd_max_workspace_bytes": (i64, []),
+            "tq_attention_workspace_bytes": (i64, [i32, i32, i32, i64]),
+            "tq_attention_decode": (i32, [P, i32, ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
+                                          ctypes.POINTER(TQConfig), ctypes.c_float, P, i32, P, i64, P]),
             "tq_lloyd_max_fit": (i32, [P, i64, i32, P, i32, P, P, P, i64, P]),
         }
         for name, (res, args) in sig.items():
@@ -363,3 +367,37 @@ def lloyd_max_fit(samples, levels: int, init, iterations: int = 500, workspace=N
     if st:
         raise TQError(st, "tq_lloyd_max_fit")
     return c, b[: levels - 1]
+
+
+# ------------------------------------------------ attention over the cache
+
+def attention_decode(q, cache, *, batch: int, width: int, kv_heads: int, head_dim: int, k_bits: int, v_bits: int,
+                     k_signed: bool = False, left_pad=None, scale: Optional[float] = None, out_dtype=None,
+                     out=None, workspace=None, stream=None):
+    """Attention of q [batch, q_heads, head_dim] over a packed batch of
+    `batch` sequences of width `width` (plane dict, as the batching ops
+    lay it out), decoding inside the kernel; left_pad is a device int32
+    tensor [batch] or None. Returns out [batch, q_heads, head_dim]."""
+    import math
+    torch = _torch()
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    q_heads = q.shape[1]
+    if out is None:
+        out = torch.empty((batch, q_heads, head_dim), dtype=out_dtype or torch.float32, device=q.device)
+    nbytes = int(lib().tq_attention_workspace_bytes(batch, q_heads, head_dim, width))
+    if nbytes < 0:
+        raise TQError(-nbytes, "tq_attention_workspace_bytes")
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if left_pad is not None and (left_pad.dtype != torch.int32 or not left_pad.is_cuda):
+        raise ValueError("left_pad must be a device int32 tensor")
+    cfg = TQConfig(head_dim, k_bits, v_bits, int(bool(k_signed)))
+    sc = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+    st = lib().tq_attention_decode(_ptr(q), _dtype_code(q), ctypes.byref(_packed(cache)), batch, width,
+                                   _ptr(left_pad), kv_heads, q_heads, ctypes.byref(cfg), sc, _ptr(out),
+                                   _dtype_code(out), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                   _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_attention_decode")
+    return out

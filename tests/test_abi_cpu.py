@@ -224,3 +224,35 @@ def test_lloyd_fit_argument_validation():
     assert L.tq_lloyd_max_fit(FAKE, 10, 4, ip, 5, cp, bp, FAKE + 4, ws, None) == tq.TQ_E_ALIGN
     bad = np.array([-1.0, 0.0, 0.0, 1.0])   # not strictly ascending
     assert L.tq_lloyd_max_fit(FAKE, 10, 4, bad.ctypes.data, 5, cp, bp, FAKE, ws, None) == tq.TQ_E_SHAPE
+
+
+def test_attention_argument_validation():
+    L = tq.lib()
+    cfg = tq.TQConfig(128, 4, 4, 0)
+    pk = _pk([FAKE] * 5)
+    by = ctypes.byref
+    ws = int(L.tq_attention_workspace_bytes(2, 8, 128, 1000))
+    assert ws == 2 * 8 * (4 * (128 + 4) + 128) * 4   # 1000 tokens: one chunk of 4 wavefront splits
+    assert L.tq_attention_workspace_bytes(2, 8, 100, 1000) < 0
+
+    def call(q=FAKE, qd=tq.TQ_F32, batch=2, width=1000, hkv=2, hq=8, c=cfg, scale=0.1, out=FAKE, od=tq.TQ_F32,
+             w=FAKE, wb=ws):
+        return L.tq_attention_decode(q, qd, by(pk), batch, width, None, hkv, hq, by(c), scale, out, od, w, wb, None)
+
+    assert call(c=tq.TQConfig(96, 4, 4, 0)) == tq.TQ_E_HEAD_DIM
+    assert call(c=tq.TQConfig(128, 4, 6, 0)) == tq.TQ_E_BITS
+    assert call(qd=5) == tq.TQ_E_DTYPE
+    assert call(od=5) == tq.TQ_E_DTYPE
+    assert call(hq=7) == tq.TQ_E_SHAPE            # not a multiple of kv heads
+    assert call(hq=6, hkv=2) == tq.TQ_E_SHAPE     # 3 query heads per KV head
+    assert call(hq=32, hkv=2) == tq.TQ_E_SHAPE    # 16 per KV head
+    assert call(scale=float("nan")) == tq.TQ_E_SHAPE
+    assert call(batch=-1) == tq.TQ_E_SHAPE
+    assert call(batch=0) == tq.TQ_OK
+    assert call(q=None) == tq.TQ_E_NULL
+    assert call(w=None) == tq.TQ_E_NULL
+    assert call(wb=ws - 1) == tq.TQ_E_SHAPE
+    assert call(q=FAKE + 4) == tq.TQ_E_ALIGN
+    assert call(out=FAKE + 8) == tq.TQ_E_ALIGN
+    assert L.tq_attention_decode(FAKE, 0, by(_pk([FAKE, FAKE, None, FAKE, FAKE])), 2, 1000, None, 2, 8, by(cfg),
+                                 0.1, FAKE, 0, FAKE, ws, None) == tq.TQ_E_NULL

@@ -1,0 +1,99 @@
+"""GPU parity of attention over the packed cache (tq_attention_decode
+through the C ABI) against the binary64 attention oracle on the codec
+oracle's decoded rows. The cache planes come from the codec oracle's
+encoder; q from seeded numpy.
+
+Tolerance: after decoding (exact: both sides use the same bf16 rows) the
+kernel computes in binary32. A score carries an absolute error of at most
+about d * 2^-24 * scale * sum_i |q_i k_i| (dot products of d terms), which
+perturbs the weights p relatively by the same amount; the weighted sums
+add at most ~(chunk + chunks) * 2^-24 relative to max |v|. For the inputs
+here (|q|, |k| ~ N(0,1) rows, scale 1/sqrt(d)) that is below 1e-5 of
+max |v| (measured: ~3e-8); the bar is 2e-5 * max|v| per element."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_quantization_tq_amd as tq
+import oracle as O
+from oracle import attention as A
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tq.lib()
+    return torch.device("cuda:0")
+
+
+def to_dev(planes, dev):
+    return {n: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev) for n, a in planes.items()}
+
+
+def case(dev, *, d, kb, vb, ks=False, g=1, hkv=2, batch=1, width=700, pads=None, seed=0, q_bf16=False,
+         out_bf16=False, scale=None, kscale=1.0):
+    print(f"[attention] d={d} k{kb}{'s' if ks else ''} v{vb} g={g} hkv={hkv} batch={batch} width={width} "
+          f"pads={pads} q_bf16={q_bf16} out_bf16={out_bf16}", flush=True)
+    rng = np.random.default_rng(seed)
+    rows = batch * width * hkv
+    k = (rng.standard_normal((rows, d)) * kscale).astype(np.float32)
+    v = rng.standard_normal((rows, d)).astype(np.float32)
+    planes = O.encode_kv(k, v, head_dim=d, k_bits=kb, v_bits=vb, k_signed=ks)
+    q = rng.standard_normal((batch, hkv * g, d)).astype(np.float32)
+    if q_bf16:
+        q = (np.round(q.view(np.uint32) / 65536.0).astype(np.uint32) << 16).view(np.float32)  # any bf16 values
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    kd, vr = A.decoded_cache(planes, rows, d, kb, vb, ks)
+    want = A.attention_decode(q.astype(np.float64), kd, vr, batch, width, pads, hkv, np.float64(np.float32(sc)))
+    qt = torch.from_numpy(q).to(dev)
+    if q_bf16:
+        qt = qt.to(torch.bfloat16)
+    lp = None if pads is None else torch.tensor(pads, dtype=torch.int32, device=dev)
+    got = tq.attention_decode(qt, to_dev(planes, dev), batch=batch, width=width, kv_heads=hkv, head_dim=d,
+                              k_bits=kb, v_bits=vb, k_signed=ks, left_pad=lp, scale=sc,
+                              out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy().astype(np.float64)
+    vmax = float(np.abs(vr).max()) if vr.size else 1.0
+    err = float(np.abs(got - want).max()) if got.size else 0.0
+    print(f"    max |err| = {err:.3e}  (max |v| = {vmax:.3f})", flush=True)
+    if out_bf16:
+        # the output's own rounding to bf16 (2^-9 relative) on top
+        assert np.all(np.abs(got - want) <= 2e-5 * vmax + 2 ** -8 * np.abs(want))
+    else:
+        assert err <= 2e-5 * vmax, err
+    return err
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+def test_head_dims_and_groups(dev, d, g):
+    case(dev, d=d, kb=4, vb=4, g=g, seed=d + g)
+
+
+@pytest.mark.parametrize("kb,vb,ks", [(2, 2, False), (3, 3, False), (5, 5, False), (8, 8, False), (8, 3, True)])
+def test_bit_widths(dev, kb, vb, ks):
+    case(dev, d=128, kb=kb, vb=vb, ks=ks, g=4, seed=10 * kb + vb)
+
+
+def test_left_padded_batch_with_an_empty_sequence(dev):
+    case(dev, d=128, kb=4, vb=4, g=2, batch=4, width=700, pads=[0, 300, 699, 700], seed=3)
+
+
+def test_many_chunks_and_dtypes(dev):
+    case(dev, d=256, kb=4, vb=5, g=4, width=5000, seed=4, q_bf16=True)
+    case(dev, d=128, kb=4, vb=4, g=4, width=1300, seed=5, out_bf16=True)
+    case(dev, d=64, kb=8, vb=2, ks=True, g=8, width=2100, seed=6, scale=0.05)
+
+
+def test_empty_cache_gives_zeros(dev):
+    q = torch.randn(2, 4, 128, device=dev)
+    planes = tq.empty_planes(0, 128, 4, 4, dev)
+    out = tq.attention_decode(q, planes, batch=2, width=0, kv_heads=2, head_dim=128, k_bits=4, v_bits=4)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)

@@ -477,7 +477,7 @@ def setup_attn_decode(torch, tq, W, dev):
     g.manual_seed(7)
     q = torch.randn((1, hq, d), generator=g, device=dev).to(torch.bfloat16)
     out = torch.empty((1, hq, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(int(tq.lib().tq_attention_workspace_bytes(1, hq, d, T)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(int(tq.lib().tq_attention_workspace_bytes(1, H, hq, d, T)), dtype=torch.uint8, device=dev)
     row_b = d * (w.k_bits + w.v_bits) // 8 + 6 * (d // 32)
     nbytes = T * H * row_b + q.numel() * 2 + out.numel() * 4
     log(f"workload attn_decode: {T} tokens x {H} KV heads, {hq} query heads, {T * H * row_b / 1e6:.1f} MB of cache")

@@ -214,7 +214,8 @@ int32_t tq_filter_rows(const tq_packed_kv *batch, int32_t b, int64_t width, cons
 
 /* Bytes of device workspace tq_attention_decode needs (host only; <0 on
  * invalid arguments). */
-int64_t tq_attention_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim, int64_t width);
+int64_t tq_attention_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t q_heads, int32_t head_dim,
+                                     int64_t width);
 
 /* q: [batch, q_heads, head_dim] of q_dtype (16-byte aligned). cache: a
  * batch of `batch` sequences of width `width` in the layout of the batching

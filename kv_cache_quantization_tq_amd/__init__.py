@@ -85,7 +85,7 @@ def lib() -> ctypes.CDLL:
             "tq_filter_rows": (i32, [ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
                                      ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
             "tq_lloyd_max_workspace_bytes": (i64, []),
-            "tq_attention_workspace_bytes": (i64, [i32, i32, i32, i64]),
+            "tq_attention_workspace_bytes": (i64, [i32, i32, i32, i32, i64]),
             "tq_attention_decode": (i32, [P, i32, ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
                                           ctypes.POINTER(TQConfig), ctypes.c_float, P, i32, P, i64, P]),
             "tq_lloyd_max_fit": (i32, [P, i64, i32, P, i32, P, P, P, i64, P]),
@@ -385,7 +385,7 @@ def attention_decode(q, cache, *, batch: int, width: int, kv_heads: int, head_di
     q_heads = q.shape[1]
     if out is None:
         out = torch.empty((batch, q_heads, head_dim), dtype=out_dtype or torch.float32, device=q.device)
-    nbytes = int(lib().tq_attention_workspace_bytes(batch, q_heads, head_dim, width))
+    nbytes = int(lib().tq_attention_workspace_bytes(batch, kv_heads, q_heads, head_dim, width))
     if nbytes < 0:
         raise TQError(-nbytes, "tq_attention_workspace_bytes")
     if workspace is None and nbytes > 0:

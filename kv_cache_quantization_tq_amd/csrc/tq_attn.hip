@@ -12,8 +12,9 @@
 // 4-bit keys and values, against 512 for a decoded bf16 cache).
 //
 // Split over the token axis (flash decoding). attn_partial_kernel: one
-// block per (sequence, chunk of kAttnChunk tokens, KV head), each of its
-// wavefronts an independent split of kWaveTokens tokens (see attn_wave).
+// block per (sequence, KV head, split of 4 * wave_tokens tokens), each of
+// its wavefronts an independent range of wave_tokens tokens (see
+// attn_wave), merged at the end of the block.
 // attn_merge_kernel merges the splits' (max, sum, output) triples;
 // attn_rotate_kernel applies the inverse rotation (the codec's transform,
 // then the sign vector). All arithmetic after decoding is binary32.
@@ -27,9 +28,9 @@
 
 namespace {
 
-constexpr int kWaveTokens = 256; // tokens per wavefront split
-constexpr int kAttnChunk = kWaveTokens * kWavesPerBlock; // tokens per block
-constexpr int kAttnMaxG = 8;    // query heads per KV head
+constexpr int kAttnMaxG = 8;         // query heads per KV head
+constexpr int kAttnTargetBlocks = 2048; // about two rounds of resident blocks on 256 CUs
+constexpr int kAttnMinWaveTokens = 32;
 
 struct AttnParams {
     const void *q;
@@ -42,11 +43,12 @@ struct AttnParams {
     float *part;
     int64_t width;
     int32_t batch, hkv, g, nsplit, q_bf16, kmode;
+    int32_t wave_tokens; // tokens per wavefront; a block (split) covers 4 wavefronts' worth
     float scale;
 };
 
-// partial results: per (sequence, query head, split) D outputs, then the
-// running max and sum (stride D + 4 keeps rows 16-byte aligned)
+// partial results: per (sequence, query head, split = block) D outputs,
+// then the running max and sum (stride D + 4 keeps rows 16-byte aligned)
 template <int D> __device__ __forceinline__ float *part_row(const AttnParams &p, int b, int h, int sp)
 {
     const int hq = p.hkv * p.g;
@@ -123,15 +125,23 @@ __device__ __forceinline__ void key_group_any(const AttnParams &p, int64_t grow,
 
 // LDS of a partial block: the query heads (shared), and per wavefront the
 // rotated values and softmax weights of its current tile
+// (rows of vt are padded by 16 bytes and the query's 32-element groups by
+// 4 floats, which spreads the 16-byte accesses of a wavefront over the LDS
+// banks)
 template <int D, int GQ> struct AttnShared {
     static constexpr int G = D / kGroup;
     static constexpr int RPW = kWave / G; // tokens per wavefront tile
-    __align__(16) float qs[GQ][D];
-    __align__(16) uint16_t vt[kWavesPerBlock][RPW][D]; // bf16 bits (the values are bf16)
+    static constexpr int VROW = D + 8;    // bf16 elements per padded vt row
+    static constexpr int QG = kGroup + 4; // floats per padded query group
+    __align__(16) float qs[GQ][G][QG];
+    __align__(16) uint16_t vt[kWavesPerBlock][RPW][VROW]; // bf16 bits (the values are bf16)
     __align__(16) float pw[kWavesPerBlock][RPW][GQ];
+    float ml[kWavesPerBlock][2];
+    // the end-of-block merge reuses vt as [4][D] floats
+    static_assert(sizeof(uint16_t) * kWavesPerBlock * RPW * D >= sizeof(float) * kWavesPerBlock * D, "merge area");
 };
 
-// Each wavefront of a block is an independent split of kWaveTokens tokens
+// Each wavefront of a block is an independent range of wave_tokens tokens
 // of one (sequence, KV head): tiles of RPW = 64 / G tokens, lane (t, grp)
 // decoding group grp of token t as the codec's decoder does; scores from
 // the lane's 32 key values against each query head (query from LDS),
@@ -145,16 +155,17 @@ __device__ __forceinline__ void attn_wave(const AttnParams &p, int b, int c, int
 {
     constexpr int G = D / kGroup;
     constexpr int RPW = AttnShared<D, GQ>::RPW;
+    constexpr int VROW = AttnShared<D, GQ>::VROW;
     constexpr int DPL = D / kWave; // output dims per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int grp = lane % G, rl = lane / G;
     const int hq = p.hkv * GQ;
     const int64_t pad = p.left_pad != nullptr ? p.left_pad[b] : 0;
-    const int64_t w0 = (int64_t)c * kAttnChunk + (int64_t)wave * kWaveTokens;
+    const int64_t w0 = ((int64_t)c * kWavesPerBlock + wave) * p.wave_tokens;
     const int64_t t_lo = w0 > pad ? w0 : pad;
-    const int64_t t_end = w0 + kWaveTokens < p.width ? w0 + kWaveTokens : p.width;
-    uint16_t (&vt)[RPW][D] = sh.vt[wave];
+    const int64_t t_end = w0 + p.wave_tokens < p.width ? w0 + p.wave_tokens : p.width;
+    uint16_t (&vt)[RPW][VROW] = sh.vt[wave];
     float (&pw)[RPW][GQ] = sh.pw[wave];
 
     float acc[DPL][GQ];
@@ -199,7 +210,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams &p, int b, int c, int
 #pragma unroll
         for (int e = 0; e < GQ; ++e) {
             float a = 0.0f;
-            const float4 *q4 = reinterpret_cast<const float4 *>(&sh.qs[e][grp * kGroup]);
+            const float4 *q4 = reinterpret_cast<const float4 *>(&sh.qs[e][grp][0]);
 #pragma unroll
             for (int u = 0; u < kGroup / 4; ++u) {
                 const float4 qv = q4[u];
@@ -240,15 +251,38 @@ __device__ __forceinline__ void attn_wave(const AttnParams &p, int b, int c, int
         wave_lds_sync();
     }
 
-    const int sp = c * kWavesPerBlock + wave;
+    // merge the block's four wavefront splits, one query head at a time,
+    // through the (now free) value area, and write the block's partial
+    float *scratch = reinterpret_cast<float *>(&sh.vt[0][0][0]); // [4][D] floats
 #pragma unroll
     for (int e = 0; e < GQ; ++e) {
-        float *r = part_row<D>(p, b, j * GQ + e, sp);
+        __syncthreads();
 #pragma unroll
-        for (int m = 0; m < DPL; ++m) r[lane + kWave * m] = acc[m][e];
+        for (int m = 0; m < DPL; ++m) scratch[wave * D + lane + kWave * m] = acc[m][e];
         if (lane == 0) {
-            r[D] = m_run[e];
-            r[D + 1] = l_run[e];
+            sh.ml[wave][0] = m_run[e];
+            sh.ml[wave][1] = l_run[e];
+        }
+        __syncthreads();
+        float M = sh.ml[0][0];
+#pragma unroll
+        for (int v = 1; v < kWavesPerBlock; ++v) M = fmaxf(M, sh.ml[v][0]);
+        float f[kWavesPerBlock], L = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kWavesPerBlock; ++v) {
+            f[v] = sh.ml[v][0] == -INFINITY ? 0.0f : expf(sh.ml[v][0] - M);
+            L = fmaf(sh.ml[v][1], f[v], L);
+        }
+        float *r = part_row<D>(p, b, j * GQ + e, c);
+        for (int i = threadIdx.x; i < D; i += kBlockThreads) {
+            float a = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kWavesPerBlock; ++v) a = fmaf(scratch[v * D + i], f[v], a);
+            r[i] = a;
+        }
+        if (threadIdx.x == 0) {
+            r[D] = M;
+            r[D + 1] = L;
         }
     }
     (void)hq;
@@ -267,7 +301,7 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     const int id = blockIdx.x;
     const int x = id % 8, r = id / 8;
     const int j = r % p.hkv;
-    const int nchunks = p.nsplit / kWavesPerBlock;
+    const int nchunks = p.nsplit;
     const int cg = (r / p.hkv) * 8 + x;
     if (cg >= p.batch * nchunks) return;
     const int b = cg / nchunks, c = cg % nchunks;
@@ -276,8 +310,8 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     for (int e = 0; e < GQ; ++e)
         for (int i = threadIdx.x; i < D; i += kBlockThreads) {
             const int64_t qi = ((int64_t)b * hq + j * GQ + e) * D + i;
-            sh.qs[e][i] = p.q_bf16 ? as_f((uint32_t)reinterpret_cast<const uint16_t *>(p.q)[qi] << 16)
-                                   : reinterpret_cast<const float *>(p.q)[qi];
+            sh.qs[e][i / kGroup][i % kGroup] = p.q_bf16 ? as_f((uint32_t)reinterpret_cast<const uint16_t *>(p.q)[qi] << 16)
+                                                        : reinterpret_cast<const float *>(p.q)[qi];
         }
     __syncthreads();
     attn_wave<D, VB, GQ>(p, b, c, j, cent, sh);
@@ -414,18 +448,35 @@ template <int D> const void *partial_kernel_for(int vb, int gq)
     }
 }
 
-int64_t n_chunks(int64_t width) { return (width + kAttnChunk - 1) / kAttnChunk; }
-int64_t n_splits(int64_t width) { return n_chunks(width) * kWavesPerBlock; }
+// Splits (blocks) per (sequence, KV head): about kAttnTargetBlocks blocks in
+// all, each wavefront taking at least kAttnMinWaveTokens tokens.
+int64_t n_splits(int32_t batch, int32_t kv_heads, int64_t width)
+{
+    if (width <= 0 || batch <= 0 || kv_heads <= 0) return 0;
+    int64_t n = (kAttnTargetBlocks + (int64_t)batch * kv_heads - 1) / ((int64_t)batch * kv_heads);
+    const int64_t most = (width + kWavesPerBlock * kAttnMinWaveTokens - 1) / (kWavesPerBlock * kAttnMinWaveTokens);
+    if (n > most) n = most;
+    return n < 1 ? 1 : n;
+}
+
+int64_t wave_tokens(int64_t width, int64_t nsplit)
+{
+    return nsplit > 0 ? (width + nsplit * kWavesPerBlock - 1) / (nsplit * kWavesPerBlock) : 0;
+}
 
 } // namespace
 
 extern "C" {
 
-int64_t tq_attention_workspace_bytes(int32_t batch, int32_t q_heads, int32_t head_dim, int64_t width)
+int64_t tq_attention_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t q_heads, int32_t head_dim,
+                                     int64_t width)
 {
-    if (batch < 0 || q_heads < 0 || width < 0 || !tq_host::valid_head_dim(head_dim)) return -TQ_E_SHAPE;
+    if (batch < 0 || kv_heads < 1 || q_heads < 0 || width < 0 || !tq_host::valid_head_dim(head_dim))
+        return -TQ_E_SHAPE;
+    if (width == 0) return 0;
     // split partials, then the merged rows
-    return (int64_t)batch * q_heads * (n_splits(width) * (head_dim + 4) + head_dim) * (int64_t)sizeof(float);
+    return (int64_t)batch * q_heads * (n_splits(batch, kv_heads, width) * (head_dim + 4) + head_dim) *
+           (int64_t)sizeof(float);
 }
 
 int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *cache, int32_t batch, int64_t width,
@@ -444,15 +495,15 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
     if (((q_heads / kv_heads) & (q_heads / kv_heads - 1)) != 0) // 1, 2, 4 or 8 query heads per KV head
         return TQ_E_SHAPE;
     if ((int64_t)batch * width * kv_heads > ((int64_t)1 << 40)) return TQ_E_SHAPE;
-    if ((int64_t)batch * n_chunks(width) > (int64_t)1 << 28) return TQ_E_SHAPE;
+
     if (batch == 0) return TQ_OK;
     const int32_t d = cfg->head_dim;
     if (q == nullptr || out == nullptr) return TQ_E_NULL;
     if (!tq_host::aligned(q, 16) || !tq_host::aligned(out, 16)) return TQ_E_ALIGN;
-    const int64_t nch = n_chunks(width);
+    const int64_t nch = n_splits(batch, kv_heads, width);
     if (width > 0) {
         if (workspace == nullptr) return TQ_E_NULL;
-        if (workspace_bytes < tq_attention_workspace_bytes(batch, q_heads, d, width)) return TQ_E_SHAPE;
+        if (workspace_bytes < tq_attention_workspace_bytes(batch, kv_heads, q_heads, d, width)) return TQ_E_SHAPE;
         if (!tq_host::aligned(workspace, 16)) return TQ_E_ALIGN;
         if (cache->k_codes == nullptr || cache->k_scale == nullptr || cache->k_zero == nullptr ||
             cache->v_codes == nullptr || cache->v_scale == nullptr)
@@ -475,7 +526,9 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
         p.batch = batch;
         p.hkv = kv_heads;
         p.g = q_heads / kv_heads;
-        p.nsplit = (int32_t)(nch * kWavesPerBlock);
+        if (wave_tokens(width, nch) > 0x7fffffff) return TQ_E_SHAPE;
+        p.nsplit = (int32_t)nch;
+        p.wave_tokens = (int32_t)wave_tokens(width, nch);
         p.q_bf16 = q_dtype == TQ_BF16;
         p.kmode = cfg->k_signed ? (8 | 16) : cfg->k_bits;
         p.scale = scale;
@@ -495,7 +548,7 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
     // merge (rows with no split are zeros), then the inverse rotation
     const int32_t rows = batch * q_heads;
     float *part = static_cast<float *>(workspace);
-    float *orot = part + (int64_t)rows * nch * kWavesPerBlock * (d + 4);
+    float *orot = part + (int64_t)rows * nch * (d + 4);
     if (width == 0) {
         // no workspace needed: every row is zero (a fill kernel, not a
         // memset, so that the call can be captured in a graph)
@@ -508,7 +561,7 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
             return TQ_E_HIP;
         return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
     }
-    int32_t nsp = (int32_t)(nch * kWavesPerBlock);
+    int32_t nsp = (int32_t)nch;
     const float *cpart = part;
     int32_t dd = d;
     void *args2[] = {&cpart, &nsp, &dd, &orot};

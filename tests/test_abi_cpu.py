@@ -231,9 +231,11 @@ def test_attention_argument_validation():
     cfg = tq.TQConfig(128, 4, 4, 0)
     pk = _pk([FAKE] * 5)
     by = ctypes.byref
-    ws = int(L.tq_attention_workspace_bytes(2, 8, 128, 1000))
-    assert ws == 2 * 8 * (4 * (128 + 4) + 128) * 4   # 1000 tokens: one chunk of 4 wavefront splits
-    assert L.tq_attention_workspace_bytes(2, 8, 100, 1000) < 0
+    ws = int(L.tq_attention_workspace_bytes(2, 2, 8, 128, 1000))
+    # 1000 tokens, 2 x 2 (sequence, KV head) pairs: at most ceil(1000 / 128) = 8 splits
+    assert ws == 2 * 8 * (8 * (128 + 4) + 128) * 4
+    assert L.tq_attention_workspace_bytes(2, 2, 8, 100, 1000) < 0
+    assert L.tq_attention_workspace_bytes(2, 2, 8, 128, 0) == 0
 
     def call(q=FAKE, qd=tq.TQ_F32, batch=2, width=1000, hkv=2, hq=8, c=cfg, scale=0.1, out=FAKE, od=tq.TQ_F32,
              w=FAKE, wb=ws):

@@ -49,6 +49,7 @@ def sources():
 # measurement taken on a kernel stays valid while these files are unchanged.
 BATCH_SOURCES = ("tq_batch.hip", "tq_host.h")
 FIT_SOURCES = ("tq_fit.hip",)
+ATTN_SOURCES = ("tq_attn.hip", "tq_device.h", "tq_host.h", "tq_tables.h")
 
 
 def kernel_sources(kind: str = "all"):
@@ -57,8 +58,10 @@ def kernel_sources(kind: str = "all"):
         files = [f for f in files if os.path.basename(f) in BATCH_SOURCES]
     elif kind == "fit":
         files = [f for f in files if os.path.basename(f) in FIT_SOURCES]
+    elif kind == "attention":
+        files = [f for f in files if os.path.basename(f) in ATTN_SOURCES]
     elif kind in ("encode", "decode", "unrotate", "codec"):
-        files = [f for f in files if os.path.basename(f) not in ("tq_batch.hip",) + FIT_SOURCES]
+        files = [f for f in files if os.path.basename(f) not in ("tq_batch.hip", "tq_attn.hip") + FIT_SOURCES]
     return files + [os.path.join(ROOT, "include", "tq.h")]
 
 

@@ -27,6 +27,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
+KINDS = ("encode", "decode", "unrotate", "merge", "fit", "attention")
+
+
 def kernel_kind(name: str) -> str:
     if "encode_kernel" in name:
         return "encode"
@@ -38,6 +41,8 @@ def kernel_kind(name: str) -> str:
         return "merge"
     if "fit_" in name and "_kernel" in name:
         return "fit"
+    if "attn_" in name and "_kernel" in name:
+        return "attention"
     if "copyBuffer" in name:
         return "copy"
     return "other"
@@ -62,7 +67,7 @@ def trace_summary(path: str, ops: dict | None = None) -> str:
     rows = []
     tr = read_trace(path)
     for name, d in tr.items():
-        if kernel_kind(name) in ("encode", "decode", "unrotate", "merge", "fit"):
+        if kernel_kind(name) in KINDS:
             rows.append((name, len(d), sum(d) / len(d), statistics.median(d), min(d)))
     lines = [f"{'kernel':70s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} {'min_us':>8s}"]
     for name, n, avg, med, mn in sorted(rows):
@@ -78,7 +83,7 @@ def stats_summary(path: str) -> str:
     with open(path) as f:
         for r in csv.DictReader(f):
             name = short_name(r["Name"])
-            if kernel_kind(name) in ("encode", "decode", "unrotate", "merge", "fit"):
+            if kernel_kind(name) in KINDS:
                 lines.append(f"{name[:70]:70s} {int(r['Calls']):5d} {float(r['AverageNs']) * 1e-3:8.2f} "
                              f"{float(r['MinNs']) * 1e-3:8.2f} {float(r['MaxNs']) * 1e-3:8.2f}")
     return "\n".join(lines)
@@ -108,7 +113,7 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, ops: dict | None = No
     w_scale = copy_kib / copy_reading(write)
     from kv_cache_quantization_tq_amd.build import source_digest
     res = {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
-    for kind in ("encode", "decode", "merge", "fit"):
+    for kind in ("encode", "decode", "merge", "fit", "attention"):
         fv = [v for n, vs in fetch.items() if kernel_kind(n) == kind for v in vs]
         wv = [v for n, vs in write.items() if kernel_kind(n) == kind for v in vs]
         if fv and wv and ops and kind in ops:

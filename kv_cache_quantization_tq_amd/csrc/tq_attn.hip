@@ -42,7 +42,7 @@ struct AttnParams {
     const int32_t *left_pad;
     float *part;
     int64_t width;
-    int32_t batch, hkv, g, nsplit, q_bf16, kmode;
+    int32_t batch, hkv, g, nsplit, q_bf16, q_terms;
     int32_t wave_tokens; // tokens per wavefront; a block (split) covers 4 wavefronts' worth
     float scale;
 };
@@ -54,8 +54,6 @@ template <int D> __device__ __forceinline__ float *part_row(const AttnParams &p,
     const int hq = p.hkv * p.g;
     return p.part + (((int64_t)b * hq + h) * p.nsplit + sp) * (D + 4);
 }
-
-__device__ __forceinline__ float bf16_round(float x) { return as_f(pack_bf16x2(x, 0.0f) << 16); }
 
 // v from the lane whose index differs in bit O (lanes exchange in pairs):
 // DPP for O = 1, 2, ds_swizzle (xor within 32 lanes) for O = 4, 8, 16,
@@ -72,249 +70,330 @@ template <int O> __device__ __forceinline__ float xor_shuffle(float v)
         return __shfl_xor(v, O);
 }
 
-// sum over the lanes whose index differs from this one's only in bits
-// [log2 LO, log2 HI) (e.g. LO = 1, HI = G: the G lanes of a token)
-template <int LO, int HI> __device__ __forceinline__ float xor_sum(float v)
-{
-    if constexpr (LO < HI) {
-        v += xor_shuffle<LO>(v);
-        return xor_sum<2 * LO, HI>(v);
-    } else {
-        return v;
-    }
-}
+// ---------------------------------------------------------------------------
+// Matrix-core operands. One wavefront tile is 16 tokens of one (sequence, KV
+// head). Lane l = 16 g + h (h = l % 16, g = l / 16):
+//
+//   scores  S[16 tokens x 16 heads] += K[tokens x 32] * Q^T[32 x heads]
+//           (v_mfma_f32_16x16x32_bf16, one per 32 of the head_dim): lane l
+//           supplies the key of token h and the query of head h, 8 elements
+//           each, elements s * D/4 + 8 c + [0, 8) for s = g (so a lane decodes
+//           one quarter of its token's key row); it receives S[tokens 4 g ..
+//           4 g + 3][head h].
+//   output  O[16 dims x 16 heads] += V^T[dims x 16 tokens] * P^T[tokens x heads]
+//           (v_mfma_f32_16x16x16_bf16, one per 16 dims and weight term): lane
+//           l supplies V[tokens 4 g .. 4 g + 3][dim h] (a transposing LDS read
+//           of the wavefront's value tile) and the weights of those same
+//           tokens for head h -- exactly the scores it received, so the
+//           softmax needs no data movement; it accumulates O[dims 4 g .. 4 g +
+//           3][head h].
+//
+// Query heads beyond the KV head's group read an all-zero row and their
+// results are never used. Keys and values are bf16 (the decoders' output
+// type), so their products are exact; the binary32 query and weights enter
+// as sums of three bf16 terms (t0 = bf16(x), t1 = bf16(x - t0), t2 =
+// bf16(x - t0 - t1), each difference exact), which keeps the contraction
+// within the rounding of binary32 arithmetic. The matrix cores accumulate
+// in binary32.
+// ---------------------------------------------------------------------------
 
-template <int LO, int HI> __device__ __forceinline__ float xor_max(float v)
-{
-    if constexpr (LO < HI) {
-        v = fmaxf(v, xor_shuffle<LO>(v));
-        return xor_max<2 * LO, HI>(v);
-    } else {
-        return v;
-    }
-}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// decodeKeys of one group, rounded to bf16
-template <int KB, bool KS>
-__device__ __forceinline__ void key_group(const AttnParams &p, int64_t grow, float (&kx)[kGroup])
-{
-    uint32_t w[KB];
-    load_codes<KB>(p.kc + grow * (4 * KB), w);
-    const float scale = f16_bits_to_f32(p.ks[grow]);
-    const float zero = f16_bits_to_f32(p.kz[grow]);
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-        const uint32_t q = unpack1<KB>(w, u);
-        const float qf = KS ? (float)(int32_t)(int8_t)(uint8_t)q : (float)q;
-        const float sum = qf + zero;
-        kx[u] = bf16_round(sum * scale);
-    }
-}
+constexpr int kTile = 16;                 // tokens per wavefront tile
+constexpr int kQRows = kAttnMaxG + 1;     // query rows in LDS; the last is zeros
+constexpr int kMaxQTerms = 3;
 
-__device__ __forceinline__ void key_group_any(const AttnParams &p, int64_t grow, float (&kx)[kGroup])
-{
-    switch (p.kmode) { // wavefront-uniform
-    case 2: key_group<2, false>(p, grow, kx); break;
-    case 3: key_group<3, false>(p, grow, kx); break;
-    case 4: key_group<4, false>(p, grow, kx); break;
-    case 5: key_group<5, false>(p, grow, kx); break;
-    case 8: key_group<8, false>(p, grow, kx); break;
-    default: key_group<8, true>(p, grow, kx); break;
-    }
-}
+// LDS layout of one wavefront's value tile (bf16): 16 token rows, each the
+// head's four quarters with 8 elements of padding after every quarter and
+// 48 after the row. Rows are then 2 D + 160 bytes apart (32 modulo 128) and
+// quarters D / 2 + 16 bytes apart (16 modulo 32): the 16-byte row writes of
+// the decoding lanes and the 8-byte transposing reads of each 16-lane group
+// fall on distinct banks.
+template <int D> struct VTile {
+    static constexpr int QE = D / 4 + 8;   // elements per padded quarter
+    static constexpr int RE = D + 80;      // elements per padded row
+    static constexpr int SPQ = D / 64;     // 16-element slices per quarter (D >= 64)
+};
+template <int D> constexpr int kQueryRow = D + 8; // elements per query row in LDS
 
-// LDS of a partial block: the query heads (shared), and per wavefront the
-// rotated values and softmax weights of its current tile
-// (rows of vt are padded by 16 bytes and the query's 32-element groups by
-// 4 floats, which spreads the 16-byte accesses of a wavefront over the LDS
-// banks)
-template <int D, int GQ> struct AttnShared {
-    static constexpr int G = D / kGroup;
-    static constexpr int RPW = kWave / G; // tokens per wavefront tile
-    static constexpr int VROW = D + 8;    // bf16 elements per padded vt row
-    static constexpr int QG = kGroup + 4; // floats per padded query group
-    __align__(16) float qs[GQ][G][QG];
-    __align__(16) uint16_t vt[kWavesPerBlock][RPW][VROW]; // bf16 bits (the values are bf16)
-    __align__(16) float pw[kWavesPerBlock][RPW][GQ];
-    float ml[kWavesPerBlock][2];
-    // the end-of-block merge reuses vt as [4][D] floats
-    static_assert(sizeof(uint16_t) * kWavesPerBlock * RPW * D >= sizeof(float) * kWavesPerBlock * D, "merge area");
+// One lane's quarter of a packed row: elements [s D/4, (s+1) D/4), held as
+// the code words of the groups it covers (a half group at D = 64, shifted so
+// that its first code is code 0) and their fp16 scales (and key zeros).
+template <int D, int B> struct Quarter {
+    static constexpr int E = D / 4;
+    static constexpr int NG = E >= kGroup ? E / kGroup : 1;
+    uint32_t w[NG][B];
+    uint16_t sc[NG], zr[NG];
 };
 
-// Each wavefront of a block is an independent range of wave_tokens tokens
-// of one (sequence, KV head): tiles of RPW = 64 / G tokens, lane (t, grp)
-// decoding group grp of token t as the codec's decoder does; scores from
-// the lane's 32 key values against each query head (query from LDS),
-// summed over the token's G lanes; online softmax over the wavefront's
-// tokens; the tile's rotated values and weights go through the
-// wavefront's LDS area, where lane l accumulates dims l, l + 64, ... of
-// every query head. Only wavefront-level synchronisation per tile.
-template <int D, int VB, int GQ>
-__device__ __forceinline__ void attn_wave(const AttnParams &p, int b, int c, int j, const float *cent,
-                                          AttnShared<D, GQ> &sh)
+template <int D, int B, bool ZERO>
+__device__ __forceinline__ void load_quarter(const uint8_t *codes, const uint16_t *scale, const uint16_t *zero,
+                                             int64_t row, int s, Quarter<D, B> &q)
 {
     constexpr int G = D / kGroup;
-    constexpr int RPW = AttnShared<D, GQ>::RPW;
-    constexpr int VROW = AttnShared<D, GQ>::VROW;
-    constexpr int DPL = D / kWave; // output dims per lane
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int grp = lane % G, rl = lane / G;
-    const int hq = p.hkv * GQ;
-    const int64_t pad = p.left_pad != nullptr ? p.left_pad[b] : 0;
-    const int64_t w0 = ((int64_t)c * kWavesPerBlock + wave) * p.wave_tokens;
-    const int64_t t_lo = w0 > pad ? w0 : pad;
-    const int64_t t_end = w0 + p.wave_tokens < p.width ? w0 + p.wave_tokens : p.width;
-    uint16_t (&vt)[RPW][VROW] = sh.vt[wave];
-    float (&pw)[RPW][GQ] = sh.pw[wave];
-
-    float acc[DPL][GQ];
-    float m_run[GQ], l_run[GQ];
+    using Q = Quarter<D, B>;
+    const uint8_t *rc = codes + row * (int64_t)(D * B / 8);
+    if constexpr (Q::E >= kGroup) {
 #pragma unroll
-    for (int m = 0; m < DPL; ++m)
+        for (int gi = 0; gi < Q::NG; ++gi) {
+            const int g = s * Q::NG + gi;
+            load_codes<B>(rc + g * (4 * B), q.w[gi]);
+            q.sc[gi] = scale[row * G + g];
+            if constexpr (ZERO) q.zr[gi] = zero[row * G + g];
+        }
+    } else {
+        const int g = s >> 1;
+        uint32_t t[B];
+        load_codes<B>(rc + g * (4 * B), t);
+        constexpr int off = kGroup / 2 * B, wo = off / 32, bs = off % 32;
+        const bool upper = (s & 1) != 0;
 #pragma unroll
-        for (int e = 0; e < GQ; ++e) acc[m][e] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < GQ; ++e) {
-        m_run[e] = -INFINITY;
-        l_run[e] = 0.0f;
+        for (int i = 0; i < B; ++i) {
+            const uint32_t lo = i + wo < B ? t[i + wo] : 0u;
+            const uint32_t hi = i + wo + 1 < B ? t[i + wo + 1] : 0u;
+            const uint32_t sh = bs != 0 ? __builtin_amdgcn_alignbit(hi, lo, bs) : lo;
+            q.w[0][i] = upper ? sh : t[i];
+        }
+        q.sc[0] = scale[row * G + g];
+        if constexpr (ZERO) q.zr[0] = zero[row * G + g];
     }
-
-    for (int64_t t0 = t_lo; t0 < t_end; t0 += RPW) {
-        const int64_t t = t0 + rl;
-        const bool valid = t < t_end;
-        const int64_t row = ((int64_t)b * p.width + (valid ? t : t_lo)) * p.hkv + j;
-        const int64_t grow = row * G + grp;
-        float kx[kGroup];
-        key_group_any(p, grow, kx);
-        // values: decodeValuesRotated (centroid * scale, bf16)
-        {
-            uint32_t w[VB];
-            load_codes<VB>(p.vc + grow * (4 * VB), w);
-            const float s = f16_bits_to_f32(p.vs[grow]);
-#pragma unroll
-            for (int u = 0; u < kGroup; u += 8) {
-                uint4 w4;
-                uint32_t *wp = &w4.x;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float a = cent[unpack1<VB>(w, u + 2 * k)] * s;
-                    const float b2 = cent[unpack1<VB>(w, u + 2 * k + 1)] * s;
-                    wp[k] = valid ? pack_bf16x2(a, b2) : 0u;
-                }
-                *reinterpret_cast<uint4 *>(&vt[rl][grp * kGroup + u]) = w4;
-            }
-        }
-        // scores, tile maximum and weights per query head
-        float alpha[GQ];
-#pragma unroll
-        for (int e = 0; e < GQ; ++e) {
-            float a = 0.0f;
-            const float4 *q4 = reinterpret_cast<const float4 *>(&sh.qs[e][grp][0]);
-#pragma unroll
-            for (int u = 0; u < kGroup / 4; ++u) {
-                const float4 qv = q4[u];
-                a = fmaf(kx[4 * u], qv.x, a);
-                a = fmaf(kx[4 * u + 1], qv.y, a);
-                a = fmaf(kx[4 * u + 2], qv.z, a);
-                a = fmaf(kx[4 * u + 3], qv.w, a);
-            }
-            a = xor_sum<1, G>(a);
-            const float sc = valid ? a * p.scale : -INFINITY;
-            const float mx = xor_max<G, kWave>(sc);
-            const float m_new = fmaxf(m_run[e], mx);
-            alpha[e] = m_new == -INFINITY ? 1.0f : expf(m_run[e] - m_new);
-            const float pe = (m_new == -INFINITY || !valid) ? 0.0f : expf(sc - m_new);
-            const float ps = xor_sum<G, kWave>(pe);
-            l_run[e] = l_run[e] * alpha[e] + ps;
-            m_run[e] = m_new;
-            if (grp == 0) pw[rl][e] = pe;
-        }
-        wave_lds_sync();
-        // weighted values of the tile
-#pragma unroll
-        for (int m = 0; m < DPL; ++m)
-#pragma unroll
-            for (int e = 0; e < GQ; ++e) acc[m][e] *= alpha[e];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            float pr[GQ];
-#pragma unroll
-            for (int e = 0; e < GQ; ++e) pr[e] = pw[r][e];
-#pragma unroll
-            for (int m = 0; m < DPL; ++m) {
-                const float v = as_f((uint32_t)vt[r][lane + kWave * m] << 16);
-#pragma unroll
-                for (int e = 0; e < GQ; ++e) acc[m][e] = fmaf(pr[e], v, acc[m][e]);
-            }
-        }
-        wave_lds_sync();
-    }
-
-    // merge the block's four wavefront splits, one query head at a time,
-    // through the (now free) value area, and write the block's partial
-    float *scratch = reinterpret_cast<float *>(&sh.vt[0][0][0]); // [4][D] floats
-#pragma unroll
-    for (int e = 0; e < GQ; ++e) {
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < DPL; ++m) scratch[wave * D + lane + kWave * m] = acc[m][e];
-        if (lane == 0) {
-            sh.ml[wave][0] = m_run[e];
-            sh.ml[wave][1] = l_run[e];
-        }
-        __syncthreads();
-        float M = sh.ml[0][0];
-#pragma unroll
-        for (int v = 1; v < kWavesPerBlock; ++v) M = fmaxf(M, sh.ml[v][0]);
-        float f[kWavesPerBlock], L = 0.0f;
-#pragma unroll
-        for (int v = 0; v < kWavesPerBlock; ++v) {
-            f[v] = sh.ml[v][0] == -INFINITY ? 0.0f : expf(sh.ml[v][0] - M);
-            L = fmaf(sh.ml[v][1], f[v], L);
-        }
-        float *r = part_row<D>(p, b, j * GQ + e, c);
-        for (int i = threadIdx.x; i < D; i += kBlockThreads) {
-            float a = 0.0f;
-#pragma unroll
-            for (int v = 0; v < kWavesPerBlock; ++v) a = fmaf(scratch[v * D + i], f[v], a);
-            r[i] = a;
-        }
-        if (threadIdx.x == 0) {
-            r[D] = M;
-            r[D + 1] = L;
-        }
-    }
-    (void)hq;
 }
+
+template <int D, int B> __device__ __forceinline__ uint32_t quarter_code(const Quarter<D, B> &q, int e)
+{
+    return unpack1<B>(q.w[Quarter<D, B>::NG > 1 ? e / kGroup : 0], e % kGroup);
+}
+
+// decodeKeys ((q + zero) * scale, rounded to bf16) of elements 8 c .. 8 c + 7
+// of the quarter, as packed bf16 pairs
+template <int D, int KB, bool KS>
+__device__ __forceinline__ u32x4_t key_chunk(const Quarter<D, KB> &k, int c, const float (&sc)[Quarter<D, KB>::NG],
+                                             const float (&zr)[Quarter<D, KB>::NG])
+{
+    const int gi = Quarter<D, KB>::NG > 1 ? 8 * c / kGroup : 0;
+    u32x4_t r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        float f[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t q = quarter_code<D, KB>(k, 8 * c + 2 * w + u);
+            const float qf = KS ? (float)(int32_t)(int8_t)(uint8_t)q : (float)q;
+            f[u] = (qf + zr[gi]) * sc[gi];
+        }
+        r[w] = pack_bf16x2(f[0], f[1]);
+    }
+    return r;
+}
+
+// decodeValuesRotated (centroid * scale, rounded to bf16) of elements 8 c ..
+// 8 c + 7 of the quarter, as packed bf16 pairs
+template <int D, int VB>
+__device__ __forceinline__ u32x4_t value_chunk(const Quarter<D, VB> &v, int c, const float *cent,
+                                               const float (&sc)[Quarter<D, VB>::NG])
+{
+    const int gi = Quarter<D, VB>::NG > 1 ? 8 * c / kGroup : 0;
+    u32x4_t r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        r[k] = pack_bf16x2(cent[quarter_code<D, VB>(v, 8 * c + 2 * k)] * sc[gi],
+                           cent[quarter_code<D, VB>(v, 8 * c + 2 * k + 1)] * sc[gi]);
+    return r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xffff0000u); }
 
 // Blocks are ordered so that the KV heads of one (sequence, chunk) are
 // dispatched to the same XCD one after another (dispatch deals block ids
 // to the 8 XCDs in turn): block id -> XCD x = id % 8, slot r = id / 8,
 // head j = r % hkv, chunk group (r / hkv) * 8 + x. The heads' rows of a
 // token are adjacent in the planes, so they share cache lines.
-template <int D, int VB, int GQ>
+//
+// Each wavefront of a block is an independent range of wave_tokens tokens
+// of one (sequence, KV head), taken in tiles of 16 tokens with an online
+// softmax per query head; the four are merged at the end of the block.
+template <int D, int VB, int KB, bool KS>
 __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams p)
 {
+    using VT = VTile<D>;
+    using KQ = Quarter<D, KB>;
+    using VQ = Quarter<D, VB>;
+    constexpr int NC = D / 32;  // 32-element chunks of the contraction (and 8-element chunks of a quarter)
+    constexpr int NS = D / 16;  // 16-dim output slices
+    constexpr int QR = kQueryRow<D>;
     __shared__ float cent[1 << VB];
-    __shared__ AttnShared<D, GQ> sh;
+    __shared__ __align__(16) uint16_t vtile[kWavesPerBlock][kTile][VT::RE];
+    __shared__ float ml[kWavesPerBlock][kAttnMaxG][2];
+    extern __shared__ __align__(16) uint16_t qlds[]; // [q_terms][kQRows][QR] bf16
+    static_assert(sizeof(float) * kWavesPerBlock * kAttnMaxG * D <= sizeof(vtile), "merge area");
+
     const int id = blockIdx.x;
     const int x = id % 8, r = id / 8;
     const int j = r % p.hkv;
-    const int nchunks = p.nsplit;
     const int cg = (r / p.hkv) * 8 + x;
-    if (cg >= p.batch * nchunks) return;
-    const int b = cg / nchunks, c = cg % nchunks;
-    const int hq = p.hkv * GQ;
-    for (int i = threadIdx.x; i < (1 << VB); i += kBlockThreads) cent[i] = dev_cent<VB>()[i];
-    for (int e = 0; e < GQ; ++e)
-        for (int i = threadIdx.x; i < D; i += kBlockThreads) {
-            const int64_t qi = ((int64_t)b * hq + j * GQ + e) * D + i;
-            sh.qs[e][i / kGroup][i % kGroup] = p.q_bf16 ? as_f((uint32_t)reinterpret_cast<const uint16_t *>(p.q)[qi] << 16)
-                                                        : reinterpret_cast<const float *>(p.q)[qi];
+    if (cg >= p.batch * p.nsplit) return;
+    const int b = cg / p.nsplit, c = cg % p.nsplit;
+    const int gq = p.g, hq = p.hkv * p.g;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < (1 << VB); i += kBlockThreads) cent[i] = dev_cent<VB>()[i];
+    for (int i = tid; i < kQRows * D; i += kBlockThreads) {
+        const int e = i / D, k = i % D;
+        float xq = 0.0f;
+        if (e < gq) {
+            const int64_t qi = ((int64_t)b * hq + j * gq + e) * D + k;
+            xq = p.q_bf16 ? as_f((uint32_t)reinterpret_cast<const uint16_t *>(p.q)[qi] << 16)
+                          : reinterpret_cast<const float *>(p.q)[qi];
         }
+        for (int t = 0; t < p.q_terms; ++t) {
+            const uint32_t w = pack_bf16x2(xq, 0.0f);
+            qlds[(t * kQRows + e) * QR + k] = (uint16_t)w;
+            xq -= bf16_lo(w);
+        }
+    }
     __syncthreads();
-    attn_wave<D, VB, GQ>(p, b, c, j, cent, sh);
+
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int h = lane & 15, g = lane >> 4;
+    const int tv = (lane & 3) | (((lane >> 3) & 3) << 2); // value-decoding lane: token tv, quarter sv
+    const int sv = ((lane >> 2) & 1) | ((lane >> 5) << 1);
+    const int64_t pad = p.left_pad != nullptr ? p.left_pad[b] : 0;
+    const int64_t w0 = ((int64_t)c * kWavesPerBlock + wave) * p.wave_tokens;
+    const int64_t t_lo = w0 > pad ? w0 : pad;
+    const int64_t t_end = w0 + p.wave_tokens < p.width ? w0 + p.wave_tokens : p.width;
+    uint16_t *vt = &vtile[wave][0][0];
+    const uint16_t *qrow = qlds + (h < gq ? h : kAttnMaxG) * QR + g * (D / 4);
+    const uint16_t *vread = vt + (4 * g + (h >> 2)) * VT::RE + 4 * (h & 3);
+    uint16_t *vwrite = vt + tv * VT::RE + sv * VT::QE;
+    const int64_t base = (int64_t)b * p.width;
+
+    f32x4_t acc[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    for (int64_t t0 = t_lo; t0 < t_end; t0 += kTile) {
+        const int64_t tk = t0 + h, tvv = t0 + tv;
+        const int64_t rowk = (base + (tk < t_end ? tk : t_lo)) * p.hkv + j;
+        const int64_t rowv = (base + (tvv < t_end ? tvv : t_lo)) * p.hkv + j;
+        KQ kq;
+        VQ vq;
+        load_quarter<D, KB, true>(p.kc, p.ks, p.kz, rowk, g, kq);
+        load_quarter<D, VB, false>(p.vc, p.vs, nullptr, rowv, sv, vq);
+
+        // scores of the tile's 16 tokens
+        float ksc[KQ::NG], kzr[KQ::NG];
+#pragma unroll
+        for (int gi = 0; gi < KQ::NG; ++gi) {
+            ksc[gi] = f16_bits_to_f32(kq.sc[gi]);
+            kzr[gi] = f16_bits_to_f32(kq.zr[gi]);
+        }
+        f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, key_chunk<D, KB, KS>(kq, cc, ksc, kzr));
+            for (int t = 0; t < p.q_terms; ++t) {
+                const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(qrow + t * (kQRows * QR) + 8 * cc);
+                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, qv), S, 0, 0, 0);
+            }
+        }
+
+        // the tile's values, bf16, into the wavefront's LDS tile
+        {
+            float vsc[VQ::NG];
+#pragma unroll
+            for (int gi = 0; gi < VQ::NG; ++gi) vsc[gi] = f16_bits_to_f32(vq.sc[gi]);
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc)
+                *reinterpret_cast<u32x4_t *>(vwrite + 8 * cc) = value_chunk<D, VB>(vq, cc, cent, vsc);
+        }
+
+        // online softmax: lane (h, g) holds tokens 4 g .. 4 g + 3 for head h
+        float s4[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s4[i] = t0 + 4 * g + i < t_end ? S[i] * p.scale : -INFINITY;
+            mx = fmaxf(mx, s4[i]);
+        }
+        mx = fmaxf(mx, xor_shuffle<16>(mx));
+        mx = fmaxf(mx, xor_shuffle<32>(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.0f : expf(m_run - m_new);
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = m_new == -INFINITY ? 0.0f : expf(s4[i] - m_new);
+        l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        m_run = m_new;
+        s16x4_t pt[kMaxQTerms];
+#pragma unroll
+        for (int t = 0; t < kMaxQTerms; ++t) {
+            const uint32_t w01 = pack_bf16x2(pr[0], pr[1]), w23 = pack_bf16x2(pr[2], pr[3]);
+            pt[t] = __builtin_bit_cast(s16x4_t, u32x2_t{w01, w23});
+            pr[0] -= bf16_lo(w01);
+            pr[1] -= bf16_hi(w01);
+            pr[2] -= bf16_lo(w23);
+            pr[3] -= bf16_hi(w23);
+        }
+        if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) acc[n] *= alpha;
+        }
+        wave_lds_sync();
+
+        // weighted values
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const uint16_t *src = vread + (n / VT::SPQ) * VT::QE + (n % VT::SPQ) * 16;
+            const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t *)(src));
+#pragma unroll
+            for (int t = 0; t < kMaxQTerms; ++t)
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pt[t], acc[n], 0, 0, 0);
+        }
+        wave_lds_sync();
+    }
+
+    // merge the block's four wavefront splits through the (now free) value
+    // tiles, [wave][head][D] floats, and write the block's partial rows
+    l_run += xor_shuffle<16>(l_run);
+    l_run += xor_shuffle<32>(l_run);
+    __syncthreads();
+    float *scr = reinterpret_cast<float *>(&vtile[0][0][0]);
+    if (h < gq) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n)
+            *reinterpret_cast<f32x4_t *>(&scr[(wave * gq + h) * D + n * 16 + 4 * g]) = acc[n];
+        if (g == 0) {
+            ml[wave][h][0] = m_run;
+            ml[wave][h][1] = l_run;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < gq * D; i += kBlockThreads) {
+        const int e = i / D, k = i % D;
+        float M = ml[0][e][0];
+#pragma unroll
+        for (int v = 1; v < kWavesPerBlock; ++v) M = fmaxf(M, ml[v][e][0]);
+        float a = 0.0f, L = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kWavesPerBlock; ++v) {
+            const float f = ml[v][e][0] == -INFINITY ? 0.0f : expf(ml[v][e][0] - M);
+            L = fmaf(ml[v][e][1], f, L);
+            a = fmaf(scr[(v * gq + e) * D + k], f, a);
+        }
+        float *row = part_row<D>(p, b, j * gq + e, c);
+        row[k] = a;
+        if (k == 0) {
+            row[D] = M;
+            row[D + 1] = L;
+        }
+    }
 }
 
 // Merge of the splits of one output row (sequence, query head), one block
@@ -427,24 +506,26 @@ __global__ void __launch_bounds__(kBlockThreads) attn_rotate_kernel(const float 
     }
 }
 
-template <int D, int VB> const void *partial_kernel_g(int gq)
+template <int D, int VB> const void *partial_kernel_k(int kmode)
 {
-    switch (gq) {
-    case 1: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 1>);
-    case 2: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 2>);
-    case 4: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 4>);
-    default: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 8>);
+    switch (kmode) {
+    case 2: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 2, false>);
+    case 3: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 3, false>);
+    case 4: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 4, false>);
+    case 5: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 5, false>);
+    case 8: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 8, false>);
+    default: return reinterpret_cast<const void *>(&attn_partial_kernel<D, VB, 8, true>);
     }
 }
 
-template <int D> const void *partial_kernel_for(int vb, int gq)
+template <int D> const void *partial_kernel_for(int vb, int kmode)
 {
     switch (vb) {
-    case 2: return partial_kernel_g<D, 2>(gq);
-    case 3: return partial_kernel_g<D, 3>(gq);
-    case 4: return partial_kernel_g<D, 4>(gq);
-    case 5: return partial_kernel_g<D, 5>(gq);
-    default: return partial_kernel_g<D, 8>(gq);
+    case 2: return partial_kernel_k<D, 2>(kmode);
+    case 3: return partial_kernel_k<D, 3>(kmode);
+    case 4: return partial_kernel_k<D, 4>(kmode);
+    case 5: return partial_kernel_k<D, 5>(kmode);
+    default: return partial_kernel_k<D, 8>(kmode);
     }
 }
 
@@ -530,19 +611,20 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
         p.nsplit = (int32_t)nch;
         p.wave_tokens = (int32_t)wave_tokens(width, nch);
         p.q_bf16 = q_dtype == TQ_BF16;
-        p.kmode = cfg->k_signed ? (8 | 16) : cfg->k_bits;
+        p.q_terms = q_dtype == TQ_BF16 ? 1 : kMaxQTerms;
         p.scale = scale;
-        const int gq = p.g;
-        const void *fn = d == 64 ? partial_kernel_for<64>(cfg->v_bits, gq)
-                       : d == 128 ? partial_kernel_for<128>(cfg->v_bits, gq)
-                       : d == 256 ? partial_kernel_for<256>(cfg->v_bits, gq)
-                                  : partial_kernel_for<512>(cfg->v_bits, gq);
+        const int kmode = cfg->k_signed ? (8 | 16) : cfg->k_bits;
+        const void *fn = d == 64 ? partial_kernel_for<64>(cfg->v_bits, kmode)
+                       : d == 128 ? partial_kernel_for<128>(cfg->v_bits, kmode)
+                       : d == 256 ? partial_kernel_for<256>(cfg->v_bits, kmode)
+                                  : partial_kernel_for<512>(cfg->v_bits, kmode);
+        const size_t qlds_bytes = (size_t)p.q_terms * kQRows * (d + 8) * sizeof(uint16_t);
         const int64_t groups = ((int64_t)batch * nch + 7) / 8;
         const int64_t blocks = groups * 8 * kv_heads;
         if (blocks > 0x7fffffff) return TQ_E_SHAPE;
         void *args[] = {&p};
-        if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kBlockThreads), args, 0, (hipStream_t)stream) !=
-            hipSuccess)
+        if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kBlockThreads), args, qlds_bytes,
+                            (hipStream_t)stream) != hipSuccess)
             return TQ_E_HIP;
     }
     // merge (rows with no split are zeros), then the inverse rotation

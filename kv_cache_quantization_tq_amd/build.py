@@ -41,6 +41,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-unit flags. The attention kernels keep their matrix-core accumulators
+# in ordinary VGPRs: with accumulation registers the compiler copies every
+# accumulator out and back on each tile around the (conditional) rescaling.
+SOURCE_FLAGS = {"tq_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -83,9 +89,9 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def _flags():
-    return HIPCC_FLAGS + shlex.split(os.environ.get("TQ_EXTRA_FLAGS", "")) + \
-        ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+def _flags(src: str = ""):
+    return HIPCC_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) + \
+        shlex.split(os.environ.get("TQ_EXTRA_FLAGS", "")) + ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
 def _run(cmd):
@@ -102,7 +108,7 @@ def build(verbose: bool = False, out: str = LIB) -> str:
         for src in sources():
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             objs.append(obj)
-            cmds.append([hipcc(), *_flags(), "-c", "-o", obj, src])
+            cmds.append([hipcc(), *_flags(src), "-c", "-o", obj, src])
         workers = min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
         with cf.ThreadPoolExecutor(workers) as ex:
             for cmd, _ in zip(cmds, ex.map(_run, cmds)):
@@ -120,7 +126,7 @@ def build(verbose: bool = False, out: str = LIB) -> str:
 def build_asm(out_dir: str) -> None:
     """Device assembly of every kernel unit (for reading the generated ISA)."""
     os.makedirs(out_dir, exist_ok=True)
-    cmds = [[hipcc(), *[f for f in _flags() if f != "-fPIC"], "--cuda-device-only", "-S",
+    cmds = [[hipcc(), *[f for f in _flags(s) if f != "-fPIC"], "--cuda-device-only", "-S",
              "-o", os.path.join(out_dir, os.path.basename(s) + ".s"), s] for s in sources()]
     with cf.ThreadPoolExecutor(8) as ex:
         list(ex.map(_run, cmds))

@@ -122,34 +122,44 @@ template <int D> constexpr int kQueryRow = D + 8; // elements per query row in L
 
 // One lane's quarter of a packed row: elements [s D/4, (s+1) D/4), held as
 // the code words of the groups it covers (a half group at D = 64, shifted so
-// that its first code is code 0) and their fp16 scales (and key zeros).
+// that its first code is code 0) and their fp16 scales (and key zeros),
+// packed two to a word when the quarter covers several groups.
 template <int D, int B> struct Quarter {
     static constexpr int E = D / 4;
     static constexpr int NG = E >= kGroup ? E / kGroup : 1;
+    static constexpr int NSW = (NG + 1) / 2; // scale words
     uint32_t w[NG][B];
-    uint16_t sc[NG], zr[NG];
+    uint32_t sc[NSW], zr[NSW];
+    __device__ __forceinline__ uint16_t scale(int gi) const { return (uint16_t)(sc[gi / 2] >> (16 * (gi & 1))); }
+    __device__ __forceinline__ uint16_t zero(int gi) const { return (uint16_t)(zr[gi / 2] >> (16 * (gi & 1))); }
 };
 
-template <int D, int B, bool ZERO>
-__device__ __forceinline__ void load_quarter(const uint8_t *codes, const uint16_t *scale, const uint16_t *zero,
-                                             int64_t row, int s, Quarter<D, B> &q)
+template <int NSW> __device__ __forceinline__ void load_scales(const uint8_t *p, uint32_t (&s)[NSW], bool pair)
 {
-    constexpr int G = D / kGroup;
+    if constexpr (NSW == 1) {
+        s[0] = pair ? *reinterpret_cast<const uint32_t *>(p) : (uint32_t)*reinterpret_cast<const uint16_t *>(p);
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        s[0] = v.x;
+        s[1] = v.y;
+    }
+}
+
+// codes from the tile's first row `codes` (uniform) at lane byte offset
+// `off` (the lane's token row plus, at D >= 128, its quarter); scales from
+// `scale` (+ `zero`) at lane byte offset `soff`
+template <int D, int B, bool ZERO>
+__device__ __forceinline__ void load_quarter(const uint8_t *codes, const uint8_t *scale, const uint8_t *zero,
+                                             uint32_t off, uint32_t soff, int s, Quarter<D, B> &q)
+{
     using Q = Quarter<D, B>;
-    const uint8_t *rc = codes + row * (int64_t)(D * B / 8);
     if constexpr (Q::E >= kGroup) {
 #pragma unroll
-        for (int gi = 0; gi < Q::NG; ++gi) {
-            const int g = s * Q::NG + gi;
-            load_codes<B>(rc + g * (4 * B), q.w[gi]);
-            q.sc[gi] = scale[row * G + g];
-            if constexpr (ZERO) q.zr[gi] = zero[row * G + g];
-        }
+        for (int gi = 0; gi < Q::NG; ++gi) load_codes<B>(codes + off + gi * (4 * B), q.w[gi]);
     } else {
-        const int g = s >> 1;
         uint32_t t[B];
-        load_codes<B>(rc + g * (4 * B), t);
-        constexpr int off = kGroup / 2 * B, wo = off / 32, bs = off % 32;
+        load_codes<B>(codes + off, t);
+        constexpr int sh_bits = kGroup / 2 * B, wo = sh_bits / 32, bs = sh_bits % 32;
         const bool upper = (s & 1) != 0;
 #pragma unroll
         for (int i = 0; i < B; ++i) {
@@ -158,14 +168,35 @@ __device__ __forceinline__ void load_quarter(const uint8_t *codes, const uint16_
             const uint32_t sh = bs != 0 ? __builtin_amdgcn_alignbit(hi, lo, bs) : lo;
             q.w[0][i] = upper ? sh : t[i];
         }
-        q.sc[0] = scale[row * G + g];
-        if constexpr (ZERO) q.zr[0] = zero[row * G + g];
     }
+    load_scales<Q::NSW>(scale + soff, q.sc, Q::NG == 2);
+    if constexpr (ZERO) load_scales<Q::NSW>(zero + soff, q.zr, Q::NG == 2);
 }
 
-template <int D, int B> __device__ __forceinline__ uint32_t quarter_code(const Quarter<D, B> &q, int e)
+// the 8 codes first .. first + 7 (first a multiple of 8) of a group's words
+// as integers; 4-bit codes are split into bytes with two masks, 8-bit codes
+// are bytes already
+template <int B> __device__ __forceinline__ void codes8(const uint32_t (&w)[B], int first, uint32_t (&c)[8])
 {
-    return unpack1<B>(q.w[Quarter<D, B>::NG > 1 ? e / kGroup : 0], e % kGroup);
+    if constexpr (B == 4) {
+        const uint32_t x = w[first / 8];
+        uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
+        // hide the masks from the optimiser, which would otherwise fold
+        // them into a shift and mask per code instead of byte selects
+        asm("" : "+v"(lo));
+        asm("" : "+v"(hi));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            c[2 * m] = (lo >> (8 * m)) & 0xffu;
+            c[2 * m + 1] = (hi >> (8 * m)) & 0xffu;
+        }
+    } else if constexpr (B == 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = (w[(first + u) / 4] >> (8 * ((first + u) % 4))) & 0xffu;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = unpack1<B>(w, first + u);
+    }
 }
 
 // decodeKeys ((q + zero) * scale, rounded to bf16) of elements 8 c .. 8 c + 7
@@ -175,14 +206,16 @@ __device__ __forceinline__ u32x4_t key_chunk(const Quarter<D, KB> &k, int c, con
                                              const float (&zr)[Quarter<D, KB>::NG])
 {
     const int gi = Quarter<D, KB>::NG > 1 ? 8 * c / kGroup : 0;
+    uint32_t q[8];
+    codes8<KB>(k.w[gi], (8 * c) % kGroup, q);
     u32x4_t r;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         float f[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const uint32_t q = quarter_code<D, KB>(k, 8 * c + 2 * w + u);
-            const float qf = KS ? (float)(int32_t)(int8_t)(uint8_t)q : (float)q;
+            const uint32_t x = q[2 * w + u];
+            const float qf = KS ? (float)(int32_t)(int8_t)(uint8_t)x : (float)x;
             f[u] = (qf + zr[gi]) * sc[gi];
         }
         r[w] = pack_bf16x2(f[0], f[1]);
@@ -197,16 +230,18 @@ __device__ __forceinline__ u32x4_t value_chunk(const Quarter<D, VB> &v, int c, c
                                                const float (&sc)[Quarter<D, VB>::NG])
 {
     const int gi = Quarter<D, VB>::NG > 1 ? 8 * c / kGroup : 0;
+    uint32_t q[8];
+    codes8<VB>(v.w[gi], (8 * c) % kGroup, q);
     u32x4_t r;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        r[k] = pack_bf16x2(cent[quarter_code<D, VB>(v, 8 * c + 2 * k)] * sc[gi],
-                           cent[quarter_code<D, VB>(v, 8 * c + 2 * k + 1)] * sc[gi]);
+    for (int k = 0; k < 4; ++k) r[k] = pack_bf16x2(cent[q[2 * k]] * sc[gi], cent[q[2 * k + 1]] * sc[gi]);
     return r;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xffff0000u); }
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Blocks are ordered so that the KV heads of one (sequence, chunk) are
 // dispatched to the same XCD one after another (dispatch deals block ids
@@ -216,16 +251,21 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xffff000
 //
 // Each wavefront of a block is an independent range of wave_tokens tokens
 // of one (sequence, KV head), taken in tiles of 16 tokens with an online
-// softmax per query head; the four are merged at the end of the block.
+// softmax per query head (in base 2: scores are scaled by scale * log2(e)
+// and exponentiated with exp2, so the running maxima and the partials'
+// maxima are base-2 logarithms); the four are merged at the end of the
+// block.
 template <int D, int VB, int KB, bool KS>
 __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams p)
 {
     using VT = VTile<D>;
     using KQ = Quarter<D, KB>;
     using VQ = Quarter<D, VB>;
+    constexpr int G = D / kGroup;
     constexpr int NC = D / 32;  // 32-element chunks of the contraction (and 8-element chunks of a quarter)
     constexpr int NS = D / 16;  // 16-dim output slices
     constexpr int QR = kQueryRow<D>;
+    constexpr uint32_t KROW = D * KB / 8, VROW = D * VB / 8; // code bytes per row
     __shared__ float cent[1 << VB];
     __shared__ __align__(16) uint16_t vtile[kWavesPerBlock][kTile][VT::RE];
     __shared__ float ml[kWavesPerBlock][kAttnMaxG][2];
@@ -270,7 +310,15 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     const uint16_t *qrow = qlds + (h < gq ? h : kAttnMaxG) * QR + g * (D / 4);
     const uint16_t *vread = vt + (4 * g + (h >> 2)) * VT::RE + 4 * (h & 3);
     uint16_t *vwrite = vt + tv * VT::RE + sv * VT::QE;
-    const int64_t base = (int64_t)b * p.width;
+    // per-token strides of the planes (a token's rows of all KV heads are
+    // adjacent) and the lanes' offsets within a token row
+    const uint32_t kstride = (uint32_t)p.hkv * KROW, vstride = (uint32_t)p.hkv * VROW;
+    const uint32_t sstride = (uint32_t)p.hkv * G * 2;
+    const uint32_t kq_off = KQ::E >= kGroup ? g * (KROW / 4) : (g >> 1) * (4 * KB);
+    const uint32_t vq_off = VQ::E >= kGroup ? sv * (VROW / 4) : (sv >> 1) * (4 * VB);
+    const uint32_t ks_off = KQ::E >= kGroup ? g * KQ::NG * 2 : (g >> 1) * 2;
+    const uint32_t vs_off = VQ::E >= kGroup ? sv * VQ::NG * 2 : (sv >> 1) * 2;
+    const float sl2 = p.scale * kLog2e;
 
     f32x4_t acc[NS];
 #pragma unroll
@@ -278,20 +326,25 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     float m_run = -INFINITY, l_run = 0.0f;
 
     for (int64_t t0 = t_lo; t0 < t_end; t0 += kTile) {
-        const int64_t tk = t0 + h, tvv = t0 + tv;
-        const int64_t rowk = (base + (tk < t_end ? tk : t_lo)) * p.hkv + j;
-        const int64_t rowv = (base + (tvv < t_end ? tvv : t_lo)) * p.hkv + j;
+        // the tile's first row (uniform) and each lane's token, clamped to
+        // the tile's last valid token
+        const int64_t row0 = ((int64_t)b * p.width + t0) * p.hkv + j;
+        const int nv = (int)(t_end - t0 < kTile ? t_end - t0 : kTile);
+        const uint32_t tk = (uint32_t)(h < nv ? h : nv - 1), tvc = (uint32_t)(tv < nv ? tv : nv - 1);
         KQ kq;
         VQ vq;
-        load_quarter<D, KB, true>(p.kc, p.ks, p.kz, rowk, g, kq);
-        load_quarter<D, VB, false>(p.vc, p.vs, nullptr, rowv, sv, vq);
+        load_quarter<D, KB, true>(p.kc + row0 * KROW, reinterpret_cast<const uint8_t *>(p.ks + row0 * G),
+                                  reinterpret_cast<const uint8_t *>(p.kz + row0 * G), tk * kstride + kq_off,
+                                  tk * sstride + ks_off, g, kq);
+        load_quarter<D, VB, false>(p.vc + row0 * VROW, reinterpret_cast<const uint8_t *>(p.vs + row0 * G), nullptr,
+                                   tvc * vstride + vq_off, tvc * sstride + vs_off, sv, vq);
 
         // scores of the tile's 16 tokens
         float ksc[KQ::NG], kzr[KQ::NG];
 #pragma unroll
         for (int gi = 0; gi < KQ::NG; ++gi) {
-            ksc[gi] = f16_bits_to_f32(kq.sc[gi]);
-            kzr[gi] = f16_bits_to_f32(kq.zr[gi]);
+            ksc[gi] = f16_bits_to_f32(kq.scale(gi));
+            kzr[gi] = f16_bits_to_f32(kq.zero(gi));
         }
         f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -307,7 +360,7 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
         {
             float vsc[VQ::NG];
 #pragma unroll
-            for (int gi = 0; gi < VQ::NG; ++gi) vsc[gi] = f16_bits_to_f32(vq.sc[gi]);
+            for (int gi = 0; gi < VQ::NG; ++gi) vsc[gi] = f16_bits_to_f32(vq.scale(gi));
 #pragma unroll
             for (int cc = 0; cc < NC; ++cc)
                 *reinterpret_cast<u32x4_t *>(vwrite + 8 * cc) = value_chunk<D, VB>(vq, cc, cent, vsc);
@@ -318,16 +371,17 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s4[i] = t0 + 4 * g + i < t_end ? S[i] * p.scale : -INFINITY;
+            s4[i] = 4 * g + i < nv ? S[i] * sl2 : -INFINITY;
             mx = fmaxf(mx, s4[i]);
         }
         mx = fmaxf(mx, xor_shuffle<16>(mx));
         mx = fmaxf(mx, xor_shuffle<32>(mx));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == -INFINITY ? 1.0f : expf(m_run - m_new);
+        const bool live = m_new != -INFINITY;
+        const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = m_new == -INFINITY ? 0.0f : expf(s4[i] - m_new);
+        for (int i = 0; i < 4; ++i) pr[i] = live ? __builtin_amdgcn_exp2f(s4[i] - m_new) : 0.0f;
         l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
         m_run = m_new;
         s16x4_t pt[kMaxQTerms];
@@ -383,7 +437,7 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
         float a = 0.0f, L = 0.0f;
 #pragma unroll
         for (int v = 0; v < kWavesPerBlock; ++v) {
-            const float f = ml[v][e][0] == -INFINITY ? 0.0f : expf(ml[v][e][0] - M);
+            const float f = ml[v][e][0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[v][e][0] - M);
             L = fmaf(ml[v][e][1], f, L);
             a = fmaf(scr[(v * gq + e) * D + k], f, a);
         }
@@ -398,8 +452,9 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
 
 // Merge of the splits of one output row (sequence, query head), one block
 // per (row, 64 dims): the largest split maximum M, the normaliser L = sum
-// l_s exp(m_s - M), and o_rot = sum o_s exp(m_s - M) / L for its dims
-// (thread (4 dims, k) sums splits k, k + 16, ...), written to `orot`.
+// l_s 2^(m_s - M), and o_rot = sum o_s 2^(m_s - M) / L for its dims (the
+// maxima are base-2; thread (4 dims, k) sums splits k, k + 16, ...),
+// written to `orot`.
 __global__ void __launch_bounds__(kBlockThreads) attn_merge_kernel(const float *part, int32_t nsplit, int32_t d,
                                                                    float *orot)
 {
@@ -422,7 +477,7 @@ __global__ void __launch_bounds__(kBlockThreads) attn_merge_kernel(const float *
     if (M != -INFINITY)
         for (int s = tid; s < nsplit; s += kBlockThreads) {
             const float ms = base[s * stride + d];
-            if (ms != -INFINITY) l = fmaf(base[s * stride + d + 1], expf(ms - M), l);
+            if (ms != -INFINITY) l = fmaf(base[s * stride + d + 1], __builtin_amdgcn_exp2f(ms - M), l);
         }
     red[tid] = l;
     __syncthreads();
@@ -438,7 +493,7 @@ __global__ void __launch_bounds__(kBlockThreads) attn_merge_kernel(const float *
             const float *ps = base + s * stride;
             const float ms = ps[d];
             if (ms == -INFINITY) continue;
-            const float f = expf(ms - M);
+            const float f = __builtin_amdgcn_exp2f(ms - M);
             const float4 v = *reinterpret_cast<const float4 *>(ps + 64 * sl + 4 * q4);
             a.x = fmaf(v.x, f, a.x);
             a.y = fmaf(v.y, f, a.y);

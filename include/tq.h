@@ -209,7 +209,10 @@ int32_t tq_filter_rows(const tq_packed_kv *batch, int32_t b, int64_t width, cons
  * KV head h / (q_heads / kv_heads):
  *   s_t = scale * <q[b,h], K_t>,  p = softmax(s),  o_rot = sum_t p_t Vrot_t,
  *   out[b,h] = unrotate(o_rot)   (normalised transform, then sign vector)
- * in binary32 after decoding. A sequence with no valid token gives zeros.
+ * in binary32 after decoding: the two contractions run on the matrix cores
+ * with binary32 accumulation, a binary32 query and the softmax weights
+ * entering as sums of three bf16 terms. A sequence with no valid token
+ * gives zeros.
  * --------------------------------------------------------------------- */
 
 /* Bytes of device workspace tq_attention_decode needs (host only; <0 on
@@ -219,13 +222,15 @@ int64_t tq_attention_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t q_
 
 /* q: [batch, q_heads, head_dim] of q_dtype (16-byte aligned). cache: a
  * batch of `batch` sequences of width `width` in the layout of the batching
- * operations above (all five planes, alignment as for tq_decode_kv);
+ * operations above (all five planes, codes aligned as for tq_decode_kv,
+ * scale and zero planes 8-byte aligned);
  * left_pad: device int32 [batch] (tokens [left_pad[b], width) of sequence
  * b are attended) or NULL for none. q_heads / kv_heads must be 1, 2, 4 or
  * 8. out: [batch, q_heads, head_dim] of out_dtype (16-byte aligned).
  * workspace: caller-owned device memory of tq_attention_workspace_bytes()
- * (16-byte aligned; may be NULL when width is 0); calls sharing a workspace
- * must not overlap. Two launches on `stream`. */
+ * (16-byte aligned; may be NULL when width is 0; its size covers every
+ * split count the call may choose); calls sharing a workspace must not
+ * overlap. Two launches on `stream` (one when width is 0). */
 int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *cache, int32_t batch, int64_t width,
                             const int32_t *left_pad, int32_t kv_heads, int32_t q_heads, const tq_config *cfg,
                             float scale, void *out, int32_t out_dtype, void *workspace, int64_t workspace_bytes,

@@ -13,14 +13,19 @@
 //
 // Split over the token axis (flash decoding). attn_partial_kernel: one
 // block per (sequence, KV head, split of 4 * wave_tokens tokens), each of
-// its wavefronts an independent range of wave_tokens tokens (see
-// attn_wave), merged at the end of the block.
-// attn_merge_kernel merges the splits' (max, sum, output) triples;
-// attn_rotate_kernel applies the inverse rotation (the codec's transform,
-// then the sign vector). All arithmetic after decoding is binary32.
+// its wavefronts an independent range of wave_tokens tokens, merged at the
+// end of the block; the contractions run on the matrix cores. The number
+// of splits fills the GPU with one round of resident blocks.
+// attn_combine_kernel merges the splits' (max, sum, output) triples of a
+// row and applies the inverse rotation (the codec's transform, then the
+// sign vector).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "tq.h"
 #include "tq_device.h"
@@ -29,7 +34,8 @@
 namespace {
 
 constexpr int kAttnMaxG = 8;         // query heads per KV head
-constexpr int kAttnTargetBlocks = 2048; // about two rounds of resident blocks on 256 CUs
+constexpr int kAttnMaxTargetBlocks = 2048; // blocks per launch aimed at, at most
+constexpr int kAttnMaxSplits = kAttnMaxTargetBlocks; // splits per (sequence, KV head), at most
 constexpr int kAttnMinWaveTokens = 32;
 
 struct AttnParams {
@@ -55,20 +61,32 @@ template <int D> __device__ __forceinline__ float *part_row(const AttnParams &p,
     return p.part + (((int64_t)b * hq + h) * p.nsplit + sp) * (D + 4);
 }
 
-// v from the lane whose index differs in bit O (lanes exchange in pairs):
-// DPP for O = 1, 2, ds_swizzle (xor within 32 lanes) for O = 4, 8, 16,
-// ds_bpermute for O = 32
-template <int O> __device__ __forceinline__ float xor_shuffle(float v)
+// max and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 with the lane
+// swaps of gfx950 (v_permlane16_swap exchanges 16-lane rows 1 and 3 of its
+// first operand with rows 0 and 2 of its second, v_permlane32_swap the upper
+// half of the first with the lower half of the second; with both operands
+// equal to x, each lane ends up holding x from itself and from its partner).
+// The second operand goes through an empty asm so that the compiler cannot
+// treat the two results as equal.
+template <bool MAX> __device__ __forceinline__ float swap_combine(float x, bool wide)
 {
-    if constexpr (O == 1)
-        return as_f((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u(v), 0xB1, 0xF, 0xF, false)); // quad_perm [1,0,3,2]
-    else if constexpr (O == 2)
-        return as_f((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u(v), 0x4E, 0xF, 0xF, false)); // quad_perm [2,3,0,1]
-    else if constexpr (O == 4 || O == 8 || O == 16)
-        return as_f((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_u(v), 0x1F | (O << 10)));
-    else
-        return __shfl_xor(v, O);
+    uint32_t a = as_u(x), c = a;
+    asm("" : "+v"(c));
+    uint32_t r0, r1;
+    if (wide) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, c, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, c, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    }
+    return MAX ? fmaxf(as_f(r0), as_f(r1)) : as_f(r0) + as_f(r1);
 }
+
+__device__ __forceinline__ float rows_max(float x) { return swap_combine<true>(swap_combine<true>(x, false), true); }
+__device__ __forceinline__ float rows_sum(float x) { return swap_combine<false>(swap_combine<false>(x, false), true); }
 
 // ---------------------------------------------------------------------------
 // Matrix-core operands. One wavefront tile is 16 tokens of one (sequence, KV
@@ -107,15 +125,14 @@ constexpr int kTile = 16;                 // tokens per wavefront tile
 constexpr int kQRows = kAttnMaxG + 1;     // query rows in LDS; the last is zeros
 constexpr int kMaxQTerms = 3;
 
-// LDS layout of one wavefront's value tile (bf16): 16 token rows, each the
-// head's four quarters with 8 elements of padding after every quarter and
-// 48 after the row. Rows are then 2 D + 160 bytes apart (32 modulo 128) and
-// quarters D / 2 + 16 bytes apart (16 modulo 32): the 16-byte row writes of
-// the decoding lanes and the 8-byte transposing reads of each 16-lane group
-// fall on distinct banks.
+// LDS layout of one wavefront's value tile (bf16): 16 token rows of D
+// elements, 2 D + 32 bytes apart (32 modulo 128), so that the 8-byte
+// transposing reads of a 16-lane group (four rows, 32 bytes each) fall on
+// distinct banks; the 16-byte row writes of the decoding lanes then meet at
+// most two to a bank.
 template <int D> struct VTile {
-    static constexpr int QE = D / 4 + 8;   // elements per padded quarter
-    static constexpr int RE = D + 80;      // elements per padded row
+    static constexpr int QE = D / 4;       // elements per quarter
+    static constexpr int RE = D + 16;      // elements per padded row
     static constexpr int SPQ = D / 64;     // 16-element slices per quarter (D >= 64)
 };
 template <int D> constexpr int kQueryRow = D + 8; // elements per query row in LDS
@@ -300,8 +317,6 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int h = lane & 15, g = lane >> 4;
-    const int tv = (lane & 3) | (((lane >> 3) & 3) << 2); // value-decoding lane: token tv, quarter sv
-    const int sv = ((lane >> 2) & 1) | ((lane >> 5) << 1);
     const int64_t pad = p.left_pad != nullptr ? p.left_pad[b] : 0;
     const int64_t w0 = ((int64_t)c * kWavesPerBlock + wave) * p.wave_tokens;
     const int64_t t_lo = w0 > pad ? w0 : pad;
@@ -309,15 +324,15 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     uint16_t *vt = &vtile[wave][0][0];
     const uint16_t *qrow = qlds + (h < gq ? h : kAttnMaxG) * QR + g * (D / 4);
     const uint16_t *vread = vt + (4 * g + (h >> 2)) * VT::RE + 4 * (h & 3);
-    uint16_t *vwrite = vt + tv * VT::RE + sv * VT::QE;
+    uint16_t *vwrite = vt + h * VT::RE + g * VT::QE;
     // per-token strides of the planes (a token's rows of all KV heads are
     // adjacent) and the lanes' offsets within a token row
     const uint32_t kstride = (uint32_t)p.hkv * KROW, vstride = (uint32_t)p.hkv * VROW;
     const uint32_t sstride = (uint32_t)p.hkv * G * 2;
     const uint32_t kq_off = KQ::E >= kGroup ? g * (KROW / 4) : (g >> 1) * (4 * KB);
-    const uint32_t vq_off = VQ::E >= kGroup ? sv * (VROW / 4) : (sv >> 1) * (4 * VB);
+    const uint32_t vq_off = VQ::E >= kGroup ? g * (VROW / 4) : (g >> 1) * (4 * VB);
     const uint32_t ks_off = KQ::E >= kGroup ? g * KQ::NG * 2 : (g >> 1) * 2;
-    const uint32_t vs_off = VQ::E >= kGroup ? sv * VQ::NG * 2 : (sv >> 1) * 2;
+    const uint32_t vs_off = VQ::E >= kGroup ? g * VQ::NG * 2 : (g >> 1) * 2;
     const float sl2 = p.scale * kLog2e;
 
     f32x4_t acc[NS];
@@ -330,14 +345,14 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
         // the tile's last valid token
         const int64_t row0 = ((int64_t)b * p.width + t0) * p.hkv + j;
         const int nv = (int)(t_end - t0 < kTile ? t_end - t0 : kTile);
-        const uint32_t tk = (uint32_t)(h < nv ? h : nv - 1), tvc = (uint32_t)(tv < nv ? tv : nv - 1);
+        const uint32_t tk = (uint32_t)(h < nv ? h : nv - 1);
         KQ kq;
         VQ vq;
         load_quarter<D, KB, true>(p.kc + row0 * KROW, reinterpret_cast<const uint8_t *>(p.ks + row0 * G),
                                   reinterpret_cast<const uint8_t *>(p.kz + row0 * G), tk * kstride + kq_off,
                                   tk * sstride + ks_off, g, kq);
         load_quarter<D, VB, false>(p.vc + row0 * VROW, reinterpret_cast<const uint8_t *>(p.vs + row0 * G), nullptr,
-                                   tvc * vstride + vq_off, tvc * sstride + vs_off, sv, vq);
+                                   tk * vstride + vq_off, tk * sstride + vs_off, g, vq);
 
         // scores of the tile's 16 tokens
         float ksc[KQ::NG], kzr[KQ::NG];
@@ -374,8 +389,7 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
             s4[i] = 4 * g + i < nv ? S[i] * sl2 : -INFINITY;
             mx = fmaxf(mx, s4[i]);
         }
-        mx = fmaxf(mx, xor_shuffle<16>(mx));
-        mx = fmaxf(mx, xor_shuffle<32>(mx));
+        mx = rows_max(mx);
         const float m_new = fmaxf(m_run, mx);
         const bool live = m_new != -INFINITY;
         const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -415,8 +429,7 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
 
     // merge the block's four wavefront splits through the (now free) value
     // tiles, [wave][head][D] floats, and write the block's partial rows
-    l_run += xor_shuffle<16>(l_run);
-    l_run += xor_shuffle<32>(l_run);
+    l_run = rows_sum(l_run);
     __syncthreads();
     float *scr = reinterpret_cast<float *>(&vtile[0][0][0]);
     if (h < gq) {
@@ -450,73 +463,87 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     }
 }
 
-// Merge of the splits of one output row (sequence, query head), one block
-// per (row, 64 dims): the largest split maximum M, the normaliser L = sum
-// l_s 2^(m_s - M), and o_rot = sum o_s 2^(m_s - M) / L for its dims (the
-// maxima are base-2; thread (4 dims, k) sums splits k, k + 16, ...),
-// written to `orot`.
-__global__ void __launch_bounds__(kBlockThreads) attn_merge_kernel(const float *part, int32_t nsplit, int32_t d,
-                                                                   float *orot)
+// One block per output row (sequence, query head): the row's split
+// partials (weighted sum o_s, base-2 maximum m_s and normaliser l_s per
+// split) merged -- the splits' maxima and normalisers are staged in LDS,
+// M = max m_s and L = sum l_s 2^(m_s - M) reduced over the block, then
+// thread (4-dim column c, split group k) sums o_s 2^(m_s - M) over splits
+// k, k + KS, ... (independent loads), the groups are added through LDS and
+// o_rot = o / L -- and the inverse rotation (the codec's transform, then
+// the sign vector) applied by the first wavefront, written as out_dtype.
+template <int D>
+__global__ void __launch_bounds__(kBlockThreads) attn_combine_kernel(const float *part, int32_t nsplit, void *out,
+                                                                     int32_t out_bf16)
 {
-    __shared__ float red[kBlockThreads];
-    __shared__ float4 acc4[16][16];
-    const int row = blockIdx.x, sl = blockIdx.y, tid = threadIdx.x;
-    const int64_t stride = d + 4;
-    const float *base = part + (int64_t)row * nsplit * stride;
+    constexpr int C4 = D / 4;              // float4 columns of a row
+    constexpr int KS = kBlockThreads / C4; // split groups
+    constexpr int G = D / kGroup;
+    __shared__ f32x4_t acc_s[KS][C4];
+    __shared__ float fs[kAttnMaxSplits];   // split maxima, then their weights 2^(m_s - M)
+    __shared__ float red[2][kWavesPerBlock];
+    __shared__ __align__(16) float orow[D];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, c = tid % C4, k = tid / C4;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const float *base = part + row * nsplit * (int64_t)(D + 4);
+
     float m = -INFINITY;
-    for (int s = tid; s < nsplit; s += kBlockThreads) m = fmaxf(m, base[s * stride + d]);
-    red[tid] = m;
-    __syncthreads();
-    for (int h = kBlockThreads / 2; h > 0; h >>= 1) {
-        if (tid < h) red[tid] = fmaxf(red[tid], red[tid + h]);
-        __syncthreads();
+    for (int sp = tid; sp < nsplit; sp += kBlockThreads) {
+        fs[sp] = base[(int64_t)sp * (D + 4) + D];
+        m = fmaxf(m, fs[sp]);
     }
-    const float M = red[0];
+    for (int o = kWave / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) red[0][wave] = m;
     __syncthreads();
+    float M = red[0][0];
+#pragma unroll
+    for (int v = 1; v < kWavesPerBlock; ++v) M = fmaxf(M, red[0][v]);
     float l = 0.0f;
-    if (M != -INFINITY)
-        for (int s = tid; s < nsplit; s += kBlockThreads) {
-            const float ms = base[s * stride + d];
-            if (ms != -INFINITY) l = fmaf(base[s * stride + d + 1], __builtin_amdgcn_exp2f(ms - M), l);
-        }
-    red[tid] = l;
-    __syncthreads();
-    for (int h = kBlockThreads / 2; h > 0; h >>= 1) {
-        if (tid < h) red[tid] += red[tid + h];
-        __syncthreads();
+    for (int sp = tid; sp < nsplit; sp += kBlockThreads) {
+        const float f = fs[sp] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fs[sp] - M);
+        fs[sp] = f;
+        l = fmaf(base[(int64_t)sp * (D + 4) + D + 1], f, l);
     }
-    const float L = red[0];
-    const int q4 = tid % 16, k = tid / 16; // dims 64 sl + 4 q4 .. + 3
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != -INFINITY)
-        for (int s = k; s < nsplit; s += 16) {
-            const float *ps = base + s * stride;
-            const float ms = ps[d];
-            if (ms == -INFINITY) continue;
-            const float f = __builtin_amdgcn_exp2f(ms - M);
-            const float4 v = *reinterpret_cast<const float4 *>(ps + 64 * sl + 4 * q4);
-            a.x = fmaf(v.x, f, a.x);
-            a.y = fmaf(v.y, f, a.y);
-            a.z = fmaf(v.z, f, a.z);
-            a.w = fmaf(v.w, f, a.w);
-        }
-    acc4[k][q4] = a;
+    for (int o = kWave / 2; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    if (lane == 0) red[1][wave] = l;
     __syncthreads();
-    if (tid < 16) {
-        float4 t = acc4[0][tid];
-        for (int kk = 1; kk < 16; ++kk) {
-            const float4 u = acc4[kk][tid];
-            t.x += u.x;
-            t.y += u.y;
-            t.z += u.z;
-            t.w += u.w;
-        }
+    f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+    for (int sp = k; sp < nsplit; sp += KS) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(base + (int64_t)sp * (D + 4) + 4 * c);
+        a += v * fs[sp];
+    }
+    acc_s[k][c] = a;
+    __syncthreads();
+    if (tid < C4) {
+        float L = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kWavesPerBlock; ++v) L += red[1][v];
+        f32x4_t o = acc_s[0][tid];
+#pragma unroll
+        for (int kk = 1; kk < KS; ++kk) o += acc_s[kk][tid];
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        t.x *= inv;
-        t.y *= inv;
-        t.z *= inv;
-        t.w *= inv;
-        *reinterpret_cast<float4 *>(orot + (int64_t)row * d + 64 * sl + 4 * tid) = t;
+        *reinterpret_cast<f32x4_t *>(&orow[4 * tid]) = o * inv;
+    }
+    __syncthreads();
+    if (tid >= kWave) return;
+    // every G-lane group of the first wavefront transforms the row; group 0 writes it
+    const int grp = tid % G;
+    float y[kGroup];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) y[u] = orow[grp * kGroup + u];
+    const Rot<D> rot(grp);
+    hadamard<D>(y, rot);
+    const uint32_t smask = dev_sign<D>(grp);
+    if (tid >= G) return;
+    if (out_bf16) {
+        uint32_t *o = reinterpret_cast<uint32_t *>(out) + (row * D + grp * kGroup) / 2;
+#pragma unroll
+        for (int w = 0; w < kGroup / 2; ++w) o[w] = pack_bf16x2(y[2 * w], y[2 * w + 1]) ^ sign_pair_mask(smask, w);
+    } else {
+        float *o = reinterpret_cast<float *>(out) + row * D + grp * kGroup;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) o[u] = ((smask >> u) & 1u) ? -y[u] : y[u];
     }
 }
 
@@ -524,41 +551,6 @@ __global__ void __launch_bounds__(kBlockThreads) attn_zero_kernel(uint32_t *out,
 {
     const int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
     if (i < words) out[i] = 0u;
-}
-
-// The inverse rotation of merged rows (transform, then sign vector), G
-// lanes per row, written as out_dtype.
-template <int D>
-__global__ void __launch_bounds__(kBlockThreads) attn_rotate_kernel(const float *orot, int32_t rows, void *out,
-                                                                    int32_t out_bf16)
-{
-    constexpr int G = D / kGroup;
-    const int grp = threadIdx.x % G;
-    const int row = (int)blockIdx.x * (kBlockThreads / G) + (int)threadIdx.x / G;
-    const int rr = row < rows ? row : rows - 1;
-    float y[kGroup];
-    const float4 *src = reinterpret_cast<const float4 *>(orot + (int64_t)rr * D + grp * kGroup);
-#pragma unroll
-    for (int u = 0; u < kGroup / 4; ++u) {
-        const float4 v = src[u];
-        y[4 * u] = v.x;
-        y[4 * u + 1] = v.y;
-        y[4 * u + 2] = v.z;
-        y[4 * u + 3] = v.w;
-    }
-    const Rot<D> rot(grp);
-    hadamard<D>(y, rot);
-    const uint32_t smask = dev_sign<D>(grp);
-    if (row >= rows) return;
-    if (out_bf16) {
-        uint32_t *o = reinterpret_cast<uint32_t *>(out) + ((int64_t)row * D + grp * kGroup) / 2;
-#pragma unroll
-        for (int k = 0; k < kGroup / 2; ++k) o[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]) ^ sign_pair_mask(smask, k);
-    } else {
-        float *o = reinterpret_cast<float *>(out) + (int64_t)row * D + grp * kGroup;
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u) o[u] = ((smask >> u) & 1u) ? -y[u] : y[u];
-    }
 }
 
 template <int D, int VB> const void *partial_kernel_k(int kmode)
@@ -584,15 +576,40 @@ template <int D> const void *partial_kernel_for(int vb, int kmode)
     }
 }
 
-// Splits (blocks) per (sequence, KV head): about kAttnTargetBlocks blocks in
-// all, each wavefront taking at least kAttnMinWaveTokens tokens.
-int64_t n_splits(int32_t batch, int32_t kv_heads, int64_t width)
+// Splits (blocks) per (sequence, KV head): about `target` blocks in all,
+// each wavefront taking at least kAttnMinWaveTokens tokens (non-decreasing
+// in `target`, so the workspace sized for kAttnMaxTargetBlocks covers every
+// launch).
+int64_t n_splits(int32_t batch, int32_t kv_heads, int64_t width, int64_t target)
 {
     if (width <= 0 || batch <= 0 || kv_heads <= 0) return 0;
-    int64_t n = (kAttnTargetBlocks + (int64_t)batch * kv_heads - 1) / ((int64_t)batch * kv_heads);
+    int64_t n = (target + (int64_t)batch * kv_heads - 1) / ((int64_t)batch * kv_heads);
     const int64_t most = (width + kWavesPerBlock * kAttnMinWaveTokens - 1) / (kWavesPerBlock * kAttnMinWaveTokens);
     if (n > most) n = most;
     return n < 1 ? 1 : n;
+}
+
+// Blocks of a partial kernel resident at once on the current device (its
+// occupancy per CU times the CU count), capped at kAttnMaxTargetBlocks: one
+// full round of blocks, so that no block waits for another to finish.
+int64_t resident_blocks(const void *fn, size_t lds_bytes)
+{
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void *, size_t>, int64_t> known;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return kAttnMaxTargetBlocks;
+    const auto key = std::make_tuple(dev, fn, lds_bytes);
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = known.find(key);
+    if (it != known.end()) return it->second;
+    int cus = 0, per_cu = 0;
+    int64_t n = kAttnMaxTargetBlocks;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlockThreads, lds_bytes) == hipSuccess &&
+        cus > 0 && per_cu > 0)
+        n = (int64_t)cus * per_cu < kAttnMaxTargetBlocks ? (int64_t)cus * per_cu : kAttnMaxTargetBlocks;
+    known[key] = n;
+    return n;
 }
 
 int64_t wave_tokens(int64_t width, int64_t nsplit)
@@ -610,8 +627,8 @@ int64_t tq_attention_workspace_bytes(int32_t batch, int32_t kv_heads, int32_t q_
     if (batch < 0 || kv_heads < 1 || q_heads < 0 || width < 0 || !tq_host::valid_head_dim(head_dim))
         return -TQ_E_SHAPE;
     if (width == 0) return 0;
-    // split partials, then the merged rows
-    return (int64_t)batch * q_heads * (n_splits(batch, kv_heads, width) * (head_dim + 4) + head_dim) *
+    // split partials: D outputs, the maximum and the normaliser per (row, split)
+    return (int64_t)batch * q_heads * n_splits(batch, kv_heads, width, kAttnMaxTargetBlocks) * (head_dim + 4) *
            (int64_t)sizeof(float);
 }
 
@@ -631,12 +648,13 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
     if (((q_heads / kv_heads) & (q_heads / kv_heads - 1)) != 0) // 1, 2, 4 or 8 query heads per KV head
         return TQ_E_SHAPE;
     if ((int64_t)batch * width * kv_heads > ((int64_t)1 << 40)) return TQ_E_SHAPE;
+    if ((int64_t)batch * q_heads > 0x7fffffff) return TQ_E_SHAPE; // one combine block per output row
 
     if (batch == 0) return TQ_OK;
     const int32_t d = cfg->head_dim;
     if (q == nullptr || out == nullptr) return TQ_E_NULL;
     if (!tq_host::aligned(q, 16) || !tq_host::aligned(out, 16)) return TQ_E_ALIGN;
-    const int64_t nch = n_splits(batch, kv_heads, width);
+    int64_t nch = 0;
     if (width > 0) {
         if (workspace == nullptr) return TQ_E_NULL;
         if (workspace_bytes < tq_attention_workspace_bytes(batch, kv_heads, q_heads, d, width)) return TQ_E_SHAPE;
@@ -646,8 +664,8 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
             return TQ_E_NULL;
         if (!tq_host::aligned(cache->k_codes, tq_host::code_align(cfg->k_bits)) ||
             !tq_host::aligned(cache->v_codes, tq_host::code_align(cfg->v_bits)) ||
-            !tq_host::aligned(cache->k_scale, 2) || !tq_host::aligned(cache->k_zero, 2) ||
-            !tq_host::aligned(cache->v_scale, 2))
+            !tq_host::aligned(cache->k_scale, 8) || !tq_host::aligned(cache->k_zero, 8) ||
+            !tq_host::aligned(cache->v_scale, 8))
             return TQ_E_ALIGN;
         AttnParams p;
         p.q = q;
@@ -662,9 +680,6 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
         p.batch = batch;
         p.hkv = kv_heads;
         p.g = q_heads / kv_heads;
-        if (wave_tokens(width, nch) > 0x7fffffff) return TQ_E_SHAPE;
-        p.nsplit = (int32_t)nch;
-        p.wave_tokens = (int32_t)wave_tokens(width, nch);
         p.q_bf16 = q_dtype == TQ_BF16;
         p.q_terms = q_dtype == TQ_BF16 ? 1 : kMaxQTerms;
         p.scale = scale;
@@ -674,6 +689,10 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
                        : d == 256 ? partial_kernel_for<256>(cfg->v_bits, kmode)
                                   : partial_kernel_for<512>(cfg->v_bits, kmode);
         const size_t qlds_bytes = (size_t)p.q_terms * kQRows * (d + 8) * sizeof(uint16_t);
+        nch = n_splits(batch, kv_heads, width, resident_blocks(fn, qlds_bytes));
+        if (nch > kAttnMaxSplits || wave_tokens(width, nch) > 0x7fffffff) return TQ_E_SHAPE;
+        p.nsplit = (int32_t)nch;
+        p.wave_tokens = (int32_t)wave_tokens(width, nch);
         const int64_t groups = ((int64_t)batch * nch + 7) / 8;
         const int64_t blocks = groups * 8 * kv_heads;
         if (blocks > 0x7fffffff) return TQ_E_SHAPE;
@@ -682,15 +701,13 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
                             (hipStream_t)stream) != hipSuccess)
             return TQ_E_HIP;
     }
-    // merge (rows with no split are zeros), then the inverse rotation
-    const int32_t rows = batch * q_heads;
-    float *part = static_cast<float *>(workspace);
-    float *orot = part + (int64_t)rows * nch * (d + 4);
+    // merge (rows with no split are zeros) and the inverse rotation
+    const int64_t rows = (int64_t)batch * q_heads;
     if (width == 0) {
         // no workspace needed: every row is zero (a fill kernel, not a
         // memset, so that the call can be captured in a graph)
         uint32_t *o32 = static_cast<uint32_t *>(out);
-        int64_t words = (int64_t)rows * d * (out_dtype == TQ_BF16 ? 2 : 4) / 4;
+        int64_t words = rows * d * (out_dtype == TQ_BF16 ? 2 : 4) / 4;
         void *argsz[] = {&o32, &words};
         if (hipLaunchKernel(reinterpret_cast<const void *>(&attn_zero_kernel),
                             dim3((uint32_t)((words + kBlockThreads - 1) / kBlockThreads)), dim3(kBlockThreads), argsz,
@@ -698,24 +715,15 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
             return TQ_E_HIP;
         return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
     }
+    const float *cpart = static_cast<const float *>(workspace);
     int32_t nsp = (int32_t)nch;
-    const float *cpart = part;
-    int32_t dd = d;
-    void *args2[] = {&cpart, &nsp, &dd, &orot};
-    if (hipLaunchKernel(reinterpret_cast<const void *>(&attn_merge_kernel), dim3((uint32_t)rows, (uint32_t)(d / 64)),
-                        dim3(kBlockThreads), args2, 0, (hipStream_t)stream) != hipSuccess)
-        return TQ_E_HIP;
-    const float *corot = orot;
-    int32_t rows32 = rows;
     int32_t obf = out_dtype == TQ_BF16;
-    void *args3[] = {&corot, &rows32, &out, &obf};
-    const int32_t rpb = kBlockThreads / (d / kGroup);
-    const void *fn3 = d == 64 ? reinterpret_cast<const void *>(&attn_rotate_kernel<64>)
-                    : d == 128 ? reinterpret_cast<const void *>(&attn_rotate_kernel<128>)
-                    : d == 256 ? reinterpret_cast<const void *>(&attn_rotate_kernel<256>)
-                    : reinterpret_cast<const void *>(&attn_rotate_kernel<512>);
-    if (hipLaunchKernel(fn3, dim3((uint32_t)((rows + rpb - 1) / rpb)), dim3(kBlockThreads), args3, 0,
-                        (hipStream_t)stream) != hipSuccess)
+    void *args2[] = {&cpart, &nsp, &out, &obf};
+    const void *fn2 = d == 64 ? reinterpret_cast<const void *>(&attn_combine_kernel<64>)
+                    : d == 128 ? reinterpret_cast<const void *>(&attn_combine_kernel<128>)
+                    : d == 256 ? reinterpret_cast<const void *>(&attn_combine_kernel<256>)
+                    : reinterpret_cast<const void *>(&attn_combine_kernel<512>);
+    if (hipLaunchKernel(fn2, dim3((uint32_t)rows), dim3(kBlockThreads), args2, 0, (hipStream_t)stream) != hipSuccess)
         return TQ_E_HIP;
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
 }

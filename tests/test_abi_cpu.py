@@ -233,7 +233,7 @@ def test_attention_argument_validation():
     by = ctypes.byref
     ws = int(L.tq_attention_workspace_bytes(2, 2, 8, 128, 1000))
     # 1000 tokens, 2 x 2 (sequence, KV head) pairs: at most ceil(1000 / 128) = 8 splits
-    assert ws == 2 * 8 * (8 * (128 + 4) + 128) * 4
+    assert ws == 2 * 8 * 8 * (128 + 4) * 4  # 8 splits of (d + 4) floats per output row
     assert L.tq_attention_workspace_bytes(2, 2, 8, 100, 1000) < 0
     assert L.tq_attention_workspace_bytes(2, 2, 8, 128, 0) == 0
 

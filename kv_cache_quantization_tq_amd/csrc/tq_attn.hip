@@ -260,20 +260,18 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xffff000
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Blocks are ordered so that the KV heads of one (sequence, chunk) are
-// dispatched to the same XCD one after another (dispatch deals block ids
-// to the 8 XCDs in turn): block id -> XCD x = id % 8, slot r = id / 8,
-// head j = r % hkv, chunk group (r / hkv) * 8 + x. The heads' rows of a
-// token are adjacent in the planes, so they share cache lines.
-//
-// Each wavefront of a block is an independent range of wave_tokens tokens
-// of one (sequence, KV head), taken in tiles of 16 tokens with an online
-// softmax per query head (in base 2: scores are scaled by scale * log2(e)
-// and exponentiated with exp2, so the running maxima and the partials'
-// maxima are base-2 logarithms); the four are merged at the end of the
-// block.
-template <int D, int VB, int KB, bool KS>
-__global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams p)
+// The tiles of one wavefront: tokens [t_lo, t_end) of (sequence b, KV
+// head j), 16 at a time, with an online softmax per query head in base 2
+// (scores scaled by scale * log2(e) and exponentiated with exp2, so the
+// running maximum is a base-2 logarithm). QT is the number of bf16 terms of
+// the query. Per tile: the 32-element chunks of keys (straight into the
+// matrix cores) and of values (into the wavefront's LDS tile) are decoded
+// in one loop, so that either's LDS waits overlap the other's arithmetic;
+// then the softmax and the weighted values.
+template <int D, int VB, int KB, bool KS, int QT>
+__device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, int64_t t_lo, int64_t t_end,
+                                           const float *cent, uint16_t *vt, const uint16_t *qrow,
+                                           f32x4_t (&acc)[D / 16], float &m_run, float &l_run)
 {
     using VT = VTile<D>;
     using KQ = Quarter<D, KB>;
@@ -283,46 +281,8 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     constexpr int NS = D / 16;  // 16-dim output slices
     constexpr int QR = kQueryRow<D>;
     constexpr uint32_t KROW = D * KB / 8, VROW = D * VB / 8; // code bytes per row
-    __shared__ float cent[1 << VB];
-    __shared__ __align__(16) uint16_t vtile[kWavesPerBlock][kTile][VT::RE];
-    __shared__ float ml[kWavesPerBlock][kAttnMaxG][2];
-    extern __shared__ __align__(16) uint16_t qlds[]; // [q_terms][kQRows][QR] bf16
-    static_assert(sizeof(float) * kWavesPerBlock * kAttnMaxG * D <= sizeof(vtile), "merge area");
-
-    const int id = blockIdx.x;
-    const int x = id % 8, r = id / 8;
-    const int j = r % p.hkv;
-    const int cg = (r / p.hkv) * 8 + x;
-    if (cg >= p.batch * p.nsplit) return;
-    const int b = cg / p.nsplit, c = cg % p.nsplit;
-    const int gq = p.g, hq = p.hkv * p.g;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < (1 << VB); i += kBlockThreads) cent[i] = dev_cent<VB>()[i];
-    for (int i = tid; i < kQRows * D; i += kBlockThreads) {
-        const int e = i / D, k = i % D;
-        float xq = 0.0f;
-        if (e < gq) {
-            const int64_t qi = ((int64_t)b * hq + j * gq + e) * D + k;
-            xq = p.q_bf16 ? as_f((uint32_t)reinterpret_cast<const uint16_t *>(p.q)[qi] << 16)
-                          : reinterpret_cast<const float *>(p.q)[qi];
-        }
-        for (int t = 0; t < p.q_terms; ++t) {
-            const uint32_t w = pack_bf16x2(xq, 0.0f);
-            qlds[(t * kQRows + e) * QR + k] = (uint16_t)w;
-            xq -= bf16_lo(w);
-        }
-    }
-    __syncthreads();
-
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
     const int h = lane & 15, g = lane >> 4;
-    const int64_t pad = p.left_pad != nullptr ? p.left_pad[b] : 0;
-    const int64_t w0 = ((int64_t)c * kWavesPerBlock + wave) * p.wave_tokens;
-    const int64_t t_lo = w0 > pad ? w0 : pad;
-    const int64_t t_end = w0 + p.wave_tokens < p.width ? w0 + p.wave_tokens : p.width;
-    uint16_t *vt = &vtile[wave][0][0];
-    const uint16_t *qrow = qlds + (h < gq ? h : kAttnMaxG) * QR + g * (D / 4);
     const uint16_t *vread = vt + (4 * g + (h >> 2)) * VT::RE + 4 * (h & 3);
     uint16_t *vwrite = vt + h * VT::RE + g * VT::QE;
     // per-token strides of the planes (a token's rows of all KV heads are
@@ -334,11 +294,6 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     const uint32_t ks_off = KQ::E >= kGroup ? g * KQ::NG * 2 : (g >> 1) * 2;
     const uint32_t vs_off = VQ::E >= kGroup ? g * VQ::NG * 2 : (g >> 1) * 2;
     const float sl2 = p.scale * kLog2e;
-
-    f32x4_t acc[NS];
-#pragma unroll
-    for (int n = 0; n < NS; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;
 
     for (int64_t t0 = t_lo; t0 < t_end; t0 += kTile) {
         // the tile's first row (uniform) and each lane's token, clamped to
@@ -354,31 +309,25 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
         load_quarter<D, VB, false>(p.vc + row0 * VROW, reinterpret_cast<const uint8_t *>(p.vs + row0 * G), nullptr,
                                    tk * vstride + vq_off, tk * sstride + vs_off, g, vq);
 
-        // scores of the tile's 16 tokens
-        float ksc[KQ::NG], kzr[KQ::NG];
+        // scores of the tile's 16 tokens; values into the LDS tile
+        float ksc[KQ::NG], kzr[KQ::NG], vsc[VQ::NG];
 #pragma unroll
         for (int gi = 0; gi < KQ::NG; ++gi) {
             ksc[gi] = f16_bits_to_f32(kq.scale(gi));
             kzr[gi] = f16_bits_to_f32(kq.zero(gi));
         }
+#pragma unroll
+        for (int gi = 0; gi < VQ::NG; ++gi) vsc[gi] = f16_bits_to_f32(vq.scale(gi));
         f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
             const bf16x8_t a = __builtin_bit_cast(bf16x8_t, key_chunk<D, KB, KS>(kq, cc, ksc, kzr));
-            for (int t = 0; t < p.q_terms; ++t) {
+#pragma unroll
+            for (int t = 0; t < QT; ++t) {
                 const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(qrow + t * (kQRows * QR) + 8 * cc);
                 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, qv), S, 0, 0, 0);
             }
-        }
-
-        // the tile's values, bf16, into the wavefront's LDS tile
-        {
-            float vsc[VQ::NG];
-#pragma unroll
-            for (int gi = 0; gi < VQ::NG; ++gi) vsc[gi] = f16_bits_to_f32(vq.scale(gi));
-#pragma unroll
-            for (int cc = 0; cc < NC; ++cc)
-                *reinterpret_cast<u32x4_t *>(vwrite + 8 * cc) = value_chunk<D, VB>(vq, cc, cent, vsc);
+            *reinterpret_cast<u32x4_t *>(vwrite + 8 * cc) = value_chunk<D, VB>(vq, cc, cent, vsc);
         }
 
         // online softmax: lane (h, g) holds tokens 4 g .. 4 g + 3 for head h
@@ -426,6 +375,70 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
         }
         wave_lds_sync();
     }
+}
+
+// Blocks are ordered so that the KV heads of one (sequence, chunk) are
+// dispatched to the same XCD one after another (dispatch deals block ids
+// to the 8 XCDs in turn): block id -> XCD x = id % 8, slot r = id / 8,
+// head j = r % hkv, chunk group (r / hkv) * 8 + x. The heads' rows of a
+// token are adjacent in the planes, so they share cache lines. Each
+// wavefront of a block is an independent range of wave_tokens tokens (see
+// wave_tiles); the four are merged at the end of the block.
+template <int D, int VB, int KB, bool KS>
+__global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams p)
+{
+    using VT = VTile<D>;
+    constexpr int NS = D / 16;  // 16-dim output slices
+    constexpr int QR = kQueryRow<D>;
+    __shared__ float cent[1 << VB];
+    __shared__ __align__(16) uint16_t vtile[kWavesPerBlock][kTile][VT::RE];
+    __shared__ float ml[kWavesPerBlock][kAttnMaxG][2];
+    extern __shared__ __align__(16) uint16_t qlds[]; // [q_terms][kQRows][QR] bf16
+    static_assert(sizeof(float) * kWavesPerBlock * kAttnMaxG * D <= sizeof(vtile), "merge area");
+
+    const int id = blockIdx.x;
+    const int x = id % 8, r = id / 8;
+    const int j = r % p.hkv;
+    const int cg = (r / p.hkv) * 8 + x;
+    if (cg >= p.batch * p.nsplit) return;
+    const int b = cg / p.nsplit, c = cg % p.nsplit;
+    const int gq = p.g, hq = p.hkv * p.g;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < (1 << VB); i += kBlockThreads) cent[i] = dev_cent<VB>()[i];
+    for (int i = tid; i < kQRows * D; i += kBlockThreads) {
+        const int e = i / D, k = i % D;
+        float xq = 0.0f;
+        if (e < gq) {
+            const int64_t qi = ((int64_t)b * hq + j * gq + e) * D + k;
+            xq = p.q_bf16 ? as_f((uint32_t)reinterpret_cast<const uint16_t *>(p.q)[qi] << 16)
+                          : reinterpret_cast<const float *>(p.q)[qi];
+        }
+        for (int t = 0; t < p.q_terms; ++t) {
+            const uint32_t w = pack_bf16x2(xq, 0.0f);
+            qlds[(t * kQRows + e) * QR + k] = (uint16_t)w;
+            xq -= bf16_lo(w);
+        }
+    }
+    __syncthreads();
+
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int h = lane & 15, g = lane >> 4;
+    const int64_t pad = p.left_pad != nullptr ? p.left_pad[b] : 0;
+    const int64_t w0 = ((int64_t)c * kWavesPerBlock + wave) * p.wave_tokens;
+    const int64_t t_lo = w0 > pad ? w0 : pad;
+    const int64_t t_end = w0 + p.wave_tokens < p.width ? w0 + p.wave_tokens : p.width;
+    const uint16_t *qrow = qlds + (h < gq ? h : kAttnMaxG) * QR + g * (D / 4);
+
+    f32x4_t acc[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    if (p.q_terms == 1)
+        wave_tiles<D, VB, KB, KS, 1>(p, b, j, t_lo, t_end, cent, &vtile[wave][0][0], qrow, acc, m_run, l_run);
+    else
+        wave_tiles<D, VB, KB, KS, kMaxQTerms>(p, b, j, t_lo, t_end, cent, &vtile[wave][0][0], qrow, acc, m_run,
+                                              l_run);
 
     // merge the block's four wavefront splits through the (now free) value
     // tiles, [wave][head][D] floats, and write the block's partial rows

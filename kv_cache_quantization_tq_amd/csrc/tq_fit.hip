@@ -37,8 +37,8 @@ constexpr int kFitBlocks = 1024; // most blocks of a pass (per-block partials be
 // of every XCD would serialise), reduced by the next step.
 struct FitWork {
     double cent[kMaxLevels];
-    unsigned long long part_sum[kFitBlocks][kMaxLevels]; // two's complement int64
-    unsigned int part_cnt[kFitBlocks][kMaxLevels];
+    unsigned long long part_sum[kMaxLevels][kFitBlocks]; // two's complement int64, level-major
+    unsigned int part_cnt[kMaxLevels][kFitBlocks];
     unsigned int part_max[kFitBlocks];                   // largest |x| bits per block
     int shift;                                           // s, or -1 when the samples cannot be fitted
 };
@@ -118,8 +118,51 @@ __host__ __device__ inline int fit_replicas(int levels)
     return r;
 }
 
+// Number of boundaries below v (levels <= 2^NS; bnd padded with +inf):
+// a binary search of NS steps, step t comparing with boundary k + 2^(NS-1-t)
+// - 1. The first RS steps select their boundary from registers (rb holds
+// the 2^RS - 1 boundaries they can need, rb[2^t - 1 + j] for step t and
+// j = k >> (NS - t)); later steps read LDS.
+template <int NS, int RS>
+__device__ __forceinline__ int search_bins(float v, const float *bnd, const float (&rb)[(1 << RS) - 1])
+{
+    int k = 0;
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+        const int st = 1 << (NS - 1 - t);
+        float bb;
+        if (t < RS) {
+            const int j = k >> (NS - t);
+            bb = rb[(1 << t) - 1];
+#pragma unroll
+            for (int c = 1; c < (1 << t); ++c) bb = j == c ? rb[(1 << t) - 1 + c] : bb;
+        } else {
+            bb = bnd[k + st - 1];
+        }
+        k += bb < v ? st : 0;
+    }
+    return k;
+}
+
+// rint(x * 2^s) as an int64. With MAGIC (every |x * 2^s| < 2^51, which the
+// shift rule guarantees for n >= 2^11): x * 2^s + 1.5 * 2^52 in binary64 is
+// rounded to an integer, half to even, in one fma (the product is exact),
+// and the integer is the difference of the bit patterns.
+template <bool MAGIC> __device__ __forceinline__ long long fixed_point(float x, int s)
+{
+    if constexpr (MAGIC) {
+        constexpr double kMagic = 6755399441055744.0; // 1.5 * 2^52
+        const double t = __builtin_fma((double)x, ldexp(1.0, s), kMagic);
+        return (long long)(__builtin_bit_cast(unsigned long long, t) - __builtin_bit_cast(unsigned long long, kMagic));
+    } else {
+        return (long long)rint(ldexp((double)x, s));
+    }
+}
+
+template <int NS, bool MAGIC>
 __global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x, int64_t n, int levels, FitWork *w)
 {
+    constexpr int RS = NS < 2 ? NS : 2;
     __shared__ float bnd[kMaxLevels];
     __shared__ unsigned long long hsum[kHistEntries];
     __shared__ unsigned int hcnt[kHistEntries];
@@ -133,24 +176,22 @@ __global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x,
         hcnt[j] = 0;
     }
     __syncthreads();
-    // binary search over the sorted boundaries (padded with +inf): the
-    // first step is the largest power of two below `levels`
-    int top = 1;
-    while (top * 2 < levels) top *= 2;
+    float rb[(1 << RS) - 1];
+#pragma unroll
+    for (int t = 0; t < RS; ++t)
+#pragma unroll
+        for (int j = 0; j < (1 << t); ++j) rb[(1 << t) - 1 + j] = bnd[(2 * j + 1) * (1 << (NS - 1 - t)) - 1];
     const int rep = (threadIdx.x & 63) % R;
     // four samples at a time (one 16-byte vector per thread and step when
     // the samples are 16-byte aligned), so that their searches overlap
     auto add4 = [&](const float (&v)[4], int valid) {
-        int k[4] = {0, 0, 0, 0};
-        for (int step = top; step > 0; step >>= 1) {
+        int k[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (bnd[k[u] + step - 1] < v[u]) k[u] += step;
-        }
+        for (int u = 0; u < 4; ++u) k[u] = search_bins<NS, RS>(v[u], bnd, rb);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (u < valid) {
-                const long long q = (long long)rint(ldexp((double)v[u], s));
+                const long long q = fixed_point<MAGIC>(v[u], s);
                 atomicAdd(&hsum[k[u] * R + rep], (unsigned long long)q);
                 atomicAdd(&hcnt[k[u] * R + rep], 1u);
             }
@@ -192,36 +233,59 @@ __global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x,
         __syncthreads();
     }
     for (int kk = threadIdx.x; kk < levels; kk += kFitThreads) {
-        w->part_sum[blockIdx.x][kk] = hsum[kk * R];
-        w->part_cnt[blockIdx.x][kk] = hcnt[kk * R];
+        w->part_sum[kk][blockIdx.x] = hsum[kk * R];
+        w->part_cnt[kk][blockIdx.x] = hcnt[kk * R];
     }
 }
 
-// one block per level: the level's total over the pass's block partials,
-// then its new centroid (a level with no sample keeps its value)
+// one block per level: the level's total over the pass's block partials
+// (contiguous, level-major; each thread loads its few independently), then
+// its new centroid (a level with no sample keeps its value)
 __global__ void __launch_bounds__(kFitThreads) fit_update_kernel(FitWork *w, int blocks)
 {
-    __shared__ unsigned long long rs[kFitThreads];
-    __shared__ unsigned long long rc[kFitThreads];
+    __shared__ unsigned long long rs[kFitThreads / 64][2];
     const int s = w->shift;
     if (s < 0) return;
-    const int k = blockIdx.x;
+    const int k = blockIdx.x, tid = threadIdx.x;
     unsigned long long sm = 0, c = 0;
-    for (int b = threadIdx.x; b < blocks; b += kFitThreads) {
-        sm += w->part_sum[b][k];
-        c += w->part_cnt[b][k];
-    }
-    rs[threadIdx.x] = sm;
-    rc[threadIdx.x] = c;
-    __syncthreads();
-    for (int h = kFitThreads / 2; h > 0; h >>= 1) {
-        if (threadIdx.x < h) {
-            rs[threadIdx.x] += rs[threadIdx.x + h];
-            rc[threadIdx.x] += rc[threadIdx.x + h];
+#pragma unroll
+    for (int i = 0; i < kFitBlocks / kFitThreads; ++i) {
+        const int b = tid + i * kFitThreads;
+        if (b < blocks) {
+            sm += w->part_sum[k][b];
+            c += w->part_cnt[k][b];
         }
-        __syncthreads();
     }
-    if (threadIdx.x == 0 && rc[0] != 0) w->cent[k] = ldexp((double)(long long)rs[0], -s) / (double)rc[0];
+    for (int o = 32; o > 0; o >>= 1) {
+        sm += __shfl_xor(sm, o);
+        c += __shfl_xor(c, o);
+    }
+    if ((tid & 63) == 0) {
+        rs[tid / 64][0] = sm;
+        rs[tid / 64][1] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int v = 1; v < kFitThreads / 64; ++v) {
+            sm += rs[v][0];
+            c += rs[v][1];
+        }
+        if (c != 0) w->cent[k] = ldexp((double)(long long)sm, -s) / (double)c;
+    }
+}
+
+template <bool MAGIC> const void *assign_kernel(int ns)
+{
+    switch (ns) {
+    case 1: return reinterpret_cast<const void *>(&fit_assign_kernel<1, MAGIC>);
+    case 2: return reinterpret_cast<const void *>(&fit_assign_kernel<2, MAGIC>);
+    case 3: return reinterpret_cast<const void *>(&fit_assign_kernel<3, MAGIC>);
+    case 4: return reinterpret_cast<const void *>(&fit_assign_kernel<4, MAGIC>);
+    case 5: return reinterpret_cast<const void *>(&fit_assign_kernel<5, MAGIC>);
+    case 6: return reinterpret_cast<const void *>(&fit_assign_kernel<6, MAGIC>);
+    case 7: return reinterpret_cast<const void *>(&fit_assign_kernel<7, MAGIC>);
+    default: return reinterpret_cast<const void *>(&fit_assign_kernel<8, MAGIC>);
+    }
 }
 
 int32_t hip_ok(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_HIP; }
@@ -258,8 +322,15 @@ int32_t tq_lloyd_max_fit(const float *samples, int64_t n, int32_t levels, const 
     const int grid = (int)(want < cap ? want : cap);
     hipLaunchKernelGGL(fit_absmax_kernel, dim3(grid), dim3(kFitThreads), 0, st, samples, n, w);
     hipLaunchKernelGGL(fit_init_kernel, dim3(1), dim3(kFitThreads), 0, st, w, grid, n);
+    int ns = 1;
+    while ((1 << ns) < levels) ++ns; // levels <= 2^ns
+    const void *assign = n >= (1 << 11) ? assign_kernel<true>(ns) : assign_kernel<false>(ns);
+    int lv = levels;
     for (int32_t it = 0; it < iterations; ++it) {
-        hipLaunchKernelGGL(fit_assign_kernel, dim3(grid), dim3(kFitThreads), 0, st, samples, n, (int)levels, w);
+        const float *xs = samples;
+        int64_t nn = n;
+        void *args[] = {&xs, &nn, &lv, &w};
+        if ((r = hip_ok(hipLaunchKernel(assign, dim3(grid), dim3(kFitThreads), args, 0, st))) != TQ_OK) return r;
         hipLaunchKernelGGL(fit_update_kernel, dim3(levels), dim3(kFitThreads), 0, st, w, grid);
     }
     if ((r = hip_ok(hipGetLastError())) != TQ_OK) return r;

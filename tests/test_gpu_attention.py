@@ -101,3 +101,41 @@ def test_empty_cache_gives_zeros(dev):
     out = tq.attention_decode(q, planes, batch=2, width=0, kv_heads=2, head_dim=128, k_bits=4, v_bits=4)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+def test_full_size_bench_configuration(dev):
+    """The bench's attention workload at its full size and launch
+    configuration (131072 tokens x 8 KV heads, d 256, V5/K4, 32 bf16 query
+    heads, default scale): the same seeded K/V and query as the bench, the
+    cache encoded by the codec oracle on the CPU, three query heads (of KV
+    heads 0, 3 and 7) compared with the binary64 oracle."""
+    from kv_cache_quantization_tq_amd import workloads as W
+    w = W.WORKLOADS["long_decode"]
+    T, H, d, hq = w.tokens, w.heads, w.head_dim, 32
+    print(f"[attention] full size: {T} tokens x {H} KV heads, d={d}, v{w.v_bits}/k{w.k_bits}, {hq} query heads",
+          flush=True)
+    k, v = W.make_kv(w, dev)
+    kh = k.reshape(T * H, d).cpu().numpy()
+    vh = v.reshape(T * H, d).cpu().numpy()
+    del k, v
+    planes = O.encode_kv(kh, vh, head_dim=d, k_bits=w.k_bits, v_bits=w.v_bits)
+    del kh, vh
+    print("    oracle planes encoded", flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    q = torch.randn((1, hq, d), generator=g, device=dev).to(torch.bfloat16)
+    got = tq.attention_decode(q, to_dev(planes, dev), batch=1, width=T, kv_heads=H, head_dim=d, k_bits=w.k_bits,
+                              v_bits=w.v_bits)
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy().astype(np.float64)
+    qn = q.float().cpu().numpy().astype(np.float64)
+    sc = np.float64(np.float32(1.0 / math.sqrt(d)))
+    for h in (0, 13, 31):
+        j = h // (hq // H)
+        rows = np.arange(T) * H + j
+        kd, vr = A.decoded_cache({n: a[rows] for n, a in planes.items()}, T, d, w.k_bits, w.v_bits)
+        want = A.attention_decode(qn[:, h:h + 1, :], kd, vr, 1, T, None, 1, sc)[0, 0]
+        vmax = float(np.abs(vr).max())
+        err = float(np.abs(got[0, h] - want).max())
+        print(f"    head {h} (KV head {j}): max |err| = {err:.3e} (max |v| = {vmax:.3f})", flush=True)
+        assert err <= 2e-5 * vmax, (h, err)

@@ -123,3 +123,21 @@ def test_merge_many_sequences_large(dev):
     want, wpad, ww = B.merge_rows(hs, HEADS)
     assert (pad, w) == (wpad, ww)
     assert_same(to_host(got), want, "merge 30 sequences")
+
+
+def test_merge_bench_configuration_full_size(dev):
+    """The bench's merge at full size: 32 caches of 4096..32768 tokens x 8
+    heads (d 128, 4-bit planes) of seeded random bytes from the bench's own
+    generator, merged into one left-padded batch; every byte of every plane
+    against the oracle."""
+    from kv_cache_quantization_tq_amd import workloads as W
+    m = W.MERGE
+    lens = W.merge_lengths()
+    H, d, kb, vb = m["heads"], m["head_dim"], m["k_bits"], m["v_bits"]
+    print(f"[batching] full size: {len(lens)} caches, {sum(lens)} tokens, width {max(lens)}", flush=True)
+    caches = [W.random_planes(n, H, d, kb, vb, seed=m["seed"] * 1000 + i, device=dev) for i, n in enumerate(lens)]
+    got, pad, w = tq.merge_rows(caches, lens, heads=H, head_dim=d, k_bits=kb, v_bits=vb)
+    torch.cuda.synchronize()
+    want, wpad, ww = B.merge_rows([to_host(c) for c in caches], H)
+    assert (pad, w) == (wpad, ww)
+    assert_same(to_host(got), want, "merge of the bench's 32 caches")

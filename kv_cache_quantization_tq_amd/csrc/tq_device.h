@@ -205,6 +205,8 @@ __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(ui
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // two binary32 -> packed bf16 pair, round to nearest even
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -434,6 +436,32 @@ template <int B> __device__ __forceinline__ void load_codes(const uint8_t *p, ui
     }
 }
 
+// load_codes with the non-temporal hint: the decoder reads each packed row
+// once, so its lines need not stay in the caches
+template <int B> __device__ __forceinline__ void load_codes_stream(const uint8_t *p, uint32_t (&w)[B])
+{
+    if constexpr (B == 2) {
+        const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+        w[0] = a.x; w[1] = a.y;
+    } else if constexpr (B == 4 || B == 8) {
+#pragma unroll
+        for (int h = 0; h < B / 4; ++h) {
+            const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p) + h);
+            w[4 * h] = a.x; w[4 * h + 1] = a.y; w[4 * h + 2] = a.z; w[4 * h + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < B; ++k) w[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p) + k);
+    }
+}
+
+// one 16-byte store with the non-temporal hint
+__device__ __forceinline__ void store16_stream(uint8_t *p, const uint4 &v)
+{
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Group loads and stores (32 elements, 16-byte vectors)
 // ---------------------------------------------------------------------------
@@ -613,7 +641,10 @@ __device__ __forceinline__ void key_encode_group(const float (&x)[kGroup], uint8
 // instruction would touch 64 pieces 64 B apart. Instead each lane writes its
 // piece to a per-wavefront LDS area (pieces padded by 16 B, which keeps the
 // 16-byte LDS accesses free of bank conflicts) and the wavefront then
-// stores the tile so that each instruction covers a contiguous 1 KB.
+// stores the tile so that each instruction covers a contiguous 1 KB. The
+// stores carry the non-temporal hint: decoded rows are written once and
+// not read back by this kernel, and without the hint the dirty lines they
+// leave in the caches are written back during whatever kernel runs next.
 template <bool BF16> struct Stage {
     static constexpr int CH = BF16 ? 4 : 8;   // 16-byte chunks per lane
     static constexpr int STRIDE = CH + 1;     // padded piece, in 16-byte units
@@ -676,14 +707,12 @@ __device__ __forceinline__ void store_tile(void *base, int64_t row0, int64_t row
     if (row0 + kWave / G <= rows) {
         // whole tile in range (wave-uniform branch)
 #pragma unroll
-        for (int i = 0; i < S::CH; ++i)
-            *reinterpret_cast<uint4 *>(tile + (uint32_t)(((S::LPI * i + c_lo) * S::CH + sub) * 16)) = v[i];
+        for (int i = 0; i < S::CH; ++i) store16_stream(tile + (uint32_t)(((S::LPI * i + c_lo) * S::CH + sub) * 16), v[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < S::CH; ++i) {
             const int c = S::LPI * i + c_lo; // piece = writer lane
-            if (row0 + c / G < rows)
-                *reinterpret_cast<uint4 *>(tile + (uint32_t)((c * S::CH + sub) * 16)) = v[i];
+            if (row0 + c / G < rows) store16_stream(tile + (uint32_t)((c * S::CH + sub) * 16), v[i]);
         }
     }
 }
@@ -851,16 +880,16 @@ __device__ __forceinline__ void load_group_codes(const uint8_t *__restrict__ kc,
     constexpr int G = D / kGroup;
     const int64_t grp = (row < rows ? row : rows - 1) * G + g;
     if constexpr (KB != 0) {
-        load_codes<KB>(kc + grp * (4 * KB), c.kw);
-        c.ks = ks[grp];
-        c.kz = kz[grp];
+        load_codes_stream<KB>(kc + grp * (4 * KB), c.kw);
+        c.ks = __builtin_nontemporal_load(ks + grp);
+        c.kz = __builtin_nontemporal_load(kz + grp);
     } else {
         c.kw[0] = 0;
         c.ks = c.kz = 0;
     }
     if (hasv) {
-        load_codes<VB>(vc + grp * (4 * VB), c.vw);
-        c.vs = vs[grp];
+        load_codes_stream<VB>(vc + grp * (4 * VB), c.vw);
+        c.vs = __builtin_nontemporal_load(vs + grp);
     } else {
 #pragma unroll
         for (int k = 0; k < VB; ++k) c.vw[k] = 0;

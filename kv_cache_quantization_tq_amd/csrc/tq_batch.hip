@@ -44,9 +44,13 @@ struct SegList {
     Seg s[kMaxSegs];
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Block (x, y) moves bytes [x * kChunk, (x + 1) * kChunk) of segment y. Whole
 // 16-byte vectors when the segment's ends allow, else 4-byte words, else
 // single bytes (code rows of 3-bit values at head_dim 64 are 24 bytes).
+// Every byte is read once and written once, so loads and stores carry the
+// non-temporal hint.
 __global__ void __launch_bounds__(kThreads) segment_copy_kernel(SegList L)
 {
     const int si = blockIdx.y;
@@ -59,14 +63,26 @@ __global__ void __launch_bounds__(kThreads) segment_copy_kernel(SegList L)
                          static_cast<uintptr_t>(b1);
     const int t = threadIdx.x;
     if ((al & 15) == 0) {
-        const uint4 *s4 = reinterpret_cast<const uint4 *>(sg.src);
-        uint4 *d4 = reinterpret_cast<uint4 *>(sg.dst);
-        for (int64_t i = b0 / 16 + t; i < b1 / 16; i += kThreads)
-            d4[i] = s4 != nullptr ? s4[i] : make_uint4(0, 0, 0, 0);
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(sg.src);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(sg.dst);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const int64_t e = b1 / 16;
+        int64_t i = b0 / 16 + t;
+        // four loads in flight per thread before their stores
+        for (; i + 3 * kThreads < e; i += 4 * kThreads) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = s4 != nullptr ? __builtin_nontemporal_load(s4 + i + u * kThreads) : zero;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(v[u], d4 + i + u * kThreads);
+        }
+        for (; i < e; i += kThreads)
+            __builtin_nontemporal_store(s4 != nullptr ? __builtin_nontemporal_load(s4 + i) : zero, d4 + i);
     } else if ((al & 3) == 0) {
         const uint32_t *s1 = reinterpret_cast<const uint32_t *>(sg.src);
         uint32_t *d1 = reinterpret_cast<uint32_t *>(sg.dst);
-        for (int64_t i = b0 / 4 + t; i < b1 / 4; i += kThreads) d1[i] = s1 != nullptr ? s1[i] : 0u;
+        for (int64_t i = b0 / 4 + t; i < b1 / 4; i += kThreads)
+            __builtin_nontemporal_store(s1 != nullptr ? __builtin_nontemporal_load(s1 + i) : 0u, d1 + i);
     } else {
         for (int64_t i = b0 + t; i < b1; i += kThreads) sg.dst[i] = sg.src != nullptr ? sg.src[i] : 0;
     }

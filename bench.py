@@ -26,12 +26,20 @@ Lloyd-Max, keys 4-bit affine. What one step is:
                        long_decode cache, decoding inside the kernel (KV
                        tokens = cached tokens attended).
 
-Inputs are resident in HBM before timing starts. Prints one JSON line:
-value = KV tokens per second (one KV token = one position with K and V of
-all its heads; for the decode workloads, tokens decoded), the roofline of
-the dominant kernel (algorithmic bytes per launch / its average duration
-from HIP events recorded on the launch stream inside the timed loop), and
-the CPU oracle timed on the host as a baseline. Diagnostics go to stderr.
+Inputs are resident in HBM before timing starts. After the warm-up steps
+the K steps run twice: launched one by one with HIP events on the launch
+stream at every kernel boundary (the per-kernel figures and the roofline),
+then captured in one HIP graph and replayed once, timed between a barrier
+and synchronisations on both sides (the timed region: `ms_per_step` and
+`value`; --no-graph times the launches one by one instead, and the Lloyd
+fit, which reads its result back every step, and the merge are always
+timed that way).
+Prints one JSON line: value = KV tokens per second (one KV token = one
+position with K and V of all its heads; for the decode workloads, tokens
+decoded), the roofline of the dominant kernel (algorithmic bytes per launch
+/ its average event-timed duration, which includes the dispatch gap before
+it), and the CPU oracle timed on the host as a baseline. Diagnostics go to
+stderr.
 """
 from __future__ import annotations
 
@@ -46,6 +54,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+
+from kv_cache_quantization_tq_amd.hiprt import HipEvent, HipGraph  # noqa: E402
 
 HEADLINE_METRIC = "KV tokens/sec encode+decode (d=128, 4-bit) and achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
@@ -199,63 +209,6 @@ def cpu_baseline(w, kn, vn, do_encode, do_decode, tokens_per_row):
 # Workload steps
 # ---------------------------------------------------------------------------
 
-class HipEvent:
-    """A timing event created with hipEventDisableSystemFence: recording it
-    performs no system-scope cache write-back and invalidation, which would
-    otherwise add several microseconds to every marked step and slow the
-    kernel that follows. Calls go to the HIP runtime already loaded in the
-    process (the one the codec library and torch use)."""
-
-    _hip = None
-    DISABLE_SYSTEM_FENCE = 0x20000000
-
-    @classmethod
-    def hip(cls):
-        if cls._hip is None:
-            import ctypes
-            path = None
-            with open("/proc/self/maps") as f:
-                for ln in f:
-                    if "libamdhip64" in ln:
-                        path = ln.split()[-1]
-                        break
-            if path is None:
-                raise RuntimeError("the HIP runtime is not loaded in this process")
-            L = ctypes.CDLL(path)
-            P = ctypes.c_void_p
-            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
-            L.hipEventRecord.argtypes = [P, P]
-            L.hipEventSynchronize.argtypes = [P]
-            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
-            L.hipEventDestroy.argtypes = [P]
-            cls._hip = L
-        return cls._hip
-
-    def __init__(self, stream):
-        import ctypes
-        self._c = ctypes
-        self.stream = stream
-        self.ev = ctypes.c_void_p()
-        if self.hip().hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE) != 0:
-            raise RuntimeError("hipEventCreateWithFlags failed")
-
-    def record(self):
-        if self.hip().hipEventRecord(self.ev, self.stream) != 0:
-            raise RuntimeError("hipEventRecord failed")
-
-    def elapsed_time(self, end):
-        """Milliseconds from this event to `end` (both complete)."""
-        ms = self._c.c_float()
-        if self.hip().hipEventSynchronize(end.ev) != 0 or \
-                self.hip().hipEventElapsedTime(self._c.byref(ms), self.ev, end.ev) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return ms.value
-
-    def __del__(self):
-        if self._hip is not None and self.ev:
-            self._hip.hipEventDestroy(self.ev)
-
-
 class Timer:
     """Events on the launch stream over the timed loop: ev[i][0] marks the
     start of step i (and the end of step i - 1), ev[i][m] for m >= 1 the
@@ -403,13 +356,12 @@ def setup_batch_merge(torch, tq, W, dev):
     lens_a = np.asarray(lens, dtype=np.int64)
     cfg = TQConfig(d, kb, vb, 0)
     pk = _packed(dst)
-    stream = ctypes_stream(torch)
 
     def step(i, ev=None):
         if ev is not None:
             ev[0].record()
         st = tq.lib().tq_merge_rows(srcs, lens_a.ctypes.data, len(lens), width, H, ctypes.byref(cfg),
-                                    ctypes.byref(pk), None, stream)
+                                    ctypes.byref(pk), None, ctypes_stream(torch))
         if st:
             raise tq.TQError(st, "tq_merge_rows")
 
@@ -518,6 +470,8 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=sorted(DESCRIPTION))
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for >= 1.5 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the steps launched one by one instead of as one graph replay")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -570,15 +524,40 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # the timed region: exactly `steps` steps, with events between kernels
+    # per-kernel figures: the `steps` steps launched one by one, with events
+    # on the launch stream at every kernel boundary (each kernel's figure
+    # includes the dispatch between it and the previous launch)
     tm = Timer(torch, steps, marks)
     torch.cuda.synchronize()
     for i in range(steps):
         step(args.warmup + i, tm.ev[i])
     tm.end.record()
     torch.cuda.synchronize()
-    ms_per_step = tm.start.elapsed_time(tm.end) / steps
+    eager_ms_per_step = tm.start.elapsed_time(tm.end) / steps
     kv_tokens = sum(tokens(args.warmup + i) for i in range(steps))
+
+    # the timed region: the same `steps` steps captured in one graph and
+    # replayed once (one submission for all their kernels, as a serving loop
+    # that captures its steps runs them). Timed launch by launch instead: the
+    # Lloyd fit, which reads its result back to the host every step, and the
+    # merge, whose graph replay faulted (its launches carry 2.9 KB segment
+    # lists as kernel arguments; the cause is not established)
+    ms_per_step, timing = eager_ms_per_step, "launches"
+    if args.workload not in ("lloyd_fit", "batch_merge") and not args.no_graph:
+        graph = HipGraph(torch, lambda: [step(args.warmup + i) for i in range(steps)])
+        graph.launch()  # untimed: the first launch uploads the graph
+        graph.synchronize()
+        t0, t1 = HipEvent(graph.stream), HipEvent(graph.stream)
+        torch.cuda.synchronize()
+        t0.record()
+        graph.launch()
+        t1.record()
+        graph.synchronize()
+        torch.cuda.synchronize()
+        ms_per_step, timing = t0.elapsed_time(t1) / steps, "graph"
+        graph.close()
+        log(f"graph replay of {steps} steps: {ms_per_step * 1e3:.1f} us per step "
+            f"(launched one by one: {eager_ms_per_step * 1e3:.1f} us)")
 
     stats = {}
     for name, (a, b, nbytes) in kernels.items():
@@ -618,6 +597,7 @@ def main():
                      "algorithmic_bytes": stats[dom]["bytes"], "avg_kernel_us": stats[dom]["avg_us"]},
         "kernels": {**stats, "step": {"GBps": step_gbps, "frac": step_gbps / PEAK_HBM_GBPS},
                     "device_copy_reference_GBps": copy_gbps},
+        "timing": {"timed_region": timing, "ms_per_step_launched_one_by_one": eager_ms_per_step},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

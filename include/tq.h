@@ -168,6 +168,13 @@ int32_t tq_value_bin_host(int32_t bits, const float *z, int64_t n, uint8_t *idx)
  * call whose output holds no tokens touches no plane pointer; planes of a
  * source that contributes no tokens may be NULL. Errors (TQ_E_*) are
  * returned before any launch and leave dst untouched.
+ *
+ * Each launch carries up to 120 plane segments (source, destination,
+ * bytes) as a kernel argument; a call needs one segment per plane and
+ * per contiguous run of tokens. Capturing a call in a HIP graph has been
+ * checked only where the call makes one launch; the replay of a graph of
+ * calls making three launches each (32 merged caches) faulted on MI355X,
+ * cause not established, so launch such calls directly.
  * --------------------------------------------------------------------- */
 
 /* mergeQuantRows: stack n caches (srcs[i] holds lens[i] tokens) into dst,

@@ -1,15 +1,19 @@
 """TurboQuant KV-cache codec for AMD MI355X (gfx950).
 
 Python binding of the C ABI in ``include/tq.h`` (library ``libtq.so`` built
-from ``csrc/tq_codec.hip``). This module only allocates outputs with torch
-and marshals pointers; every step of the codec runs in the HIP kernels. If
-the library is not built, every call raises ``RuntimeError``.
+from the sources in ``csrc/`` by ``build.py``). This module only allocates
+outputs with torch and marshals pointers; every step runs in the HIP
+kernels. If the library is not built, every call raises ``RuntimeError``.
 
 Functions follow the page "@mlx-bun/inference 0.0.0-stage -> 1.0.0", ops.ts:
 ``encode_kv`` (encodeKeys / encodeValues + packBits), ``decode_kv``
 (unpackBits + decodeKeys / decodeValues, or decodeValuesRotated with
-``rotated_v=True``), ``unrotate_values`` (unrotateValues) and
-``packed_dim`` (packedDim).
+``rotated_v=True``), ``unrotate_values`` (unrotateValues),
+``attention_decode`` (attention over the packed cache, values as
+decodeValuesRotated) and ``packed_dim`` (packedDim); the page "mlx-bun
+0.0.9 -> 0.0.11": ``merge_rows``, ``extend_rows``, ``extract_row``,
+``filter_rows`` (batched-quant.ts) and ``lloyd_max_fit`` (the LLOYD_MAX
+tables' fit).
 """
 from __future__ import annotations
 
@@ -281,13 +285,14 @@ def _i64(vals):
 
 
 def merge_rows(caches, lens, *, heads: int, head_dim: int, k_bits: int, v_bits: int, k_signed: bool = False,
-               width: Optional[int] = None, stream=None):
+               width: Optional[int] = None, out: Optional[Dict] = None, stream=None):
     """Stack caches (plane dicts, cache i holding lens[i] tokens) into one
-    left-padded batch. Returns (planes, left_pad, width)."""
+    left-padded batch, written to `out` (planes for n * width tokens;
+    allocated when None). Returns (planes, left_pad, width)."""
     n = len(caches)
     lens_a = _i64(lens)
     width = int(lens_a.max()) if width is None and n else int(width or 0)
-    dst = _like(caches[0], n * width, heads, head_dim, k_bits, v_bits)
+    dst = _like(caches[0], n * width, heads, head_dim, k_bits, v_bits) if out is None else out
     srcs = (TQPackedKV * max(n, 1))(*[_packed(c) for c in caches])
     pad = _i64([0] * max(n, 1))
     cfg = TQConfig(head_dim, k_bits, v_bits, int(bool(k_signed)))

@@ -26,20 +26,17 @@ Lloyd-Max, keys 4-bit affine. What one step is:
                        long_decode cache, decoding inside the kernel (KV
                        tokens = cached tokens attended).
 
-Inputs are resident in HBM before timing starts. After the warm-up steps
-the K steps run twice: launched one by one with HIP events on the launch
-stream at every kernel boundary (the per-kernel figures and the roofline),
-then captured in one HIP graph and replayed once, timed between a barrier
-and synchronisations on both sides (the timed region: `ms_per_step` and
-`value`; --no-graph times the launches one by one instead, and the Lloyd
-fit, which reads its result back every step, and the merge are always
-timed that way).
-Prints one JSON line: value = KV tokens per second (one KV token = one
-position with K and V of all its heads; for the decode workloads, tokens
-decoded), the roofline of the dominant kernel (algorithmic bytes per launch
-/ its average event-timed duration, which includes the dispatch gap before
-it), and the CPU oracle timed on the host as a baseline. Diagnostics go to
-stderr.
+Inputs are resident in HBM before timing starts. The timed region is
+exactly K steps launched one by one after W warm-up steps, bracketed by
+synchronisations, with HIP events on the launch stream at every kernel
+boundary. Prints one JSON line: value = KV tokens per second (one KV token
+= one position with K and V of all its heads; for the decode workloads,
+tokens decoded), the roofline of the dominant kernel (algorithmic bytes per
+launch / its average event-timed duration in the timed region, which
+includes the dispatch gap before it), the CPU oracle timed on the host as a
+baseline, and `graph_replay`: the same K steps captured in one HIP graph
+and replayed once after the timed region (no dispatch gaps; not for the
+Lloyd fit or the merge; --no-graph skips it). Diagnostics go to stderr.
 """
 from __future__ import annotations
 
@@ -471,7 +468,7 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0: enough for >= 1.5 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
-                    help="time the steps launched one by one instead of as one graph replay")
+                    help="skip the graph replay of the timed steps reported alongside")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -524,28 +521,28 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # per-kernel figures: the `steps` steps launched one by one, with events
-    # on the launch stream at every kernel boundary (each kernel's figure
-    # includes the dispatch between it and the previous launch)
+    # the timed region: exactly `steps` steps launched one by one, with
+    # events on the launch stream at every kernel boundary (each kernel's
+    # figure includes the dispatch between it and the previous launch)
     tm = Timer(torch, steps, marks)
     torch.cuda.synchronize()
     for i in range(steps):
         step(args.warmup + i, tm.ev[i])
     tm.end.record()
     torch.cuda.synchronize()
-    eager_ms_per_step = tm.start.elapsed_time(tm.end) / steps
+    ms_per_step = tm.start.elapsed_time(tm.end) / steps
     kv_tokens = sum(tokens(args.warmup + i) for i in range(steps))
 
-    # the timed region: the same `steps` steps captured in one graph and
-    # replayed once (one submission for all their kernels, as a serving loop
-    # that captures its steps runs them). Timed launch by launch instead: the
-    # Lloyd fit, which reads its result back to the host every step, and the
-    # merge, whose graph replay faulted (its launches carry 2.9 KB segment
-    # lists as kernel arguments; the cause is not established)
-    ms_per_step, timing = eager_ms_per_step, "launches"
+    # reported alongside: the same `steps` steps captured in one graph and
+    # replayed once (one submission for all their kernels, no dispatch gaps),
+    # after an untimed replay that uploads the graph. Not for the Lloyd fit,
+    # which reads its result back to the host every step, nor the merge,
+    # whose graph replay faulted (its launches carry 2.9 KB segment lists as
+    # kernel arguments; the cause is not established)
+    graph_ms_per_step = None
     if args.workload not in ("lloyd_fit", "batch_merge") and not args.no_graph:
         graph = HipGraph(torch, lambda: [step(args.warmup + i) for i in range(steps)])
-        graph.launch()  # untimed: the first launch uploads the graph
+        graph.launch()
         graph.synchronize()
         t0, t1 = HipEvent(graph.stream), HipEvent(graph.stream)
         torch.cuda.synchronize()
@@ -554,10 +551,10 @@ def main():
         t1.record()
         graph.synchronize()
         torch.cuda.synchronize()
-        ms_per_step, timing = t0.elapsed_time(t1) / steps, "graph"
+        graph_ms_per_step = t0.elapsed_time(t1) / steps
         graph.close()
-        log(f"graph replay of {steps} steps: {ms_per_step * 1e3:.1f} us per step "
-            f"(launched one by one: {eager_ms_per_step * 1e3:.1f} us)")
+        log(f"graph replay of the same {steps} steps: {graph_ms_per_step * 1e3:.1f} us per step "
+            f"(timed region, launched one by one: {ms_per_step * 1e3:.1f} us)")
 
     stats = {}
     for name, (a, b, nbytes) in kernels.items():
@@ -597,7 +594,8 @@ def main():
                      "algorithmic_bytes": stats[dom]["bytes"], "avg_kernel_us": stats[dom]["avg_us"]},
         "kernels": {**stats, "step": {"GBps": step_gbps, "frac": step_gbps / PEAK_HBM_GBPS},
                     "device_copy_reference_GBps": copy_gbps},
-        "timing": {"timed_region": timing, "ms_per_step_launched_one_by_one": eager_ms_per_step},
+        "graph_replay": None if graph_ms_per_step is None else {
+            "ms_per_step": graph_ms_per_step, "value": kv_tokens / (steps * graph_ms_per_step * 1e-3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

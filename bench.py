@@ -364,16 +364,15 @@ def setup_batch_merge(torch, tq, W, dev):
 
     def cpu():
         import oracle.batching as OB
-        ns = 8  # the first 8 caches
         host = [{n: (p.cpu().numpy().view(np.uint16) if p.dtype == torch.int16 else p.cpu().numpy())
-                 for n, p in c.items()} for c in caches[:ns]]
+                 for n, p in c.items()} for c in caches]
         t0 = time.perf_counter()
         OB.merge_rows(host, H)
         t = time.perf_counter() - t0
-        ntok = sum(lens[:ns])
-        log(f"cpu oracle (merge of {ns} caches, {ntok} tokens): {t:.2f} s")
+        ntok = sum(lens)
+        log(f"cpu oracle (merge of all {len(lens)} caches, {ntok} tokens): {t:.2f} s")
         return {"value": ntok / t, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-                "sample": f"merge of the first {ns} of the 32 caches ({ntok} tokens), one thread (numpy)"}
+                "sample": f"the whole merge of the {len(lens)} caches ({ntok} tokens), one thread (numpy)"}
 
     config = {"workload": DESCRIPTION["batch_merge"], "sequences": len(lens), "tokens": sum(lens), "width": width,
               "heads": H, "head_dim": d, "v_bits": vb, "k_bits": kb}
@@ -398,7 +397,7 @@ def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
     def cpu():
         import numpy as np
         from oracle import lloyd as OL
-        ns, it = 1 << 20, 5
+        ns, it = 1 << 22, 25
         xs = x[:ns].cpu().numpy()
         t0 = time.perf_counter()
         OL.fit_samples(xs, init, it)
@@ -419,7 +418,7 @@ def setup_attn_decode(torch, tq, W, dev):
     k, v = W.make_kv(w, dev)
     planes = tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits)
     torch.cuda.synchronize()
-    ns = 8192  # tokens of the oracle sample
+    ns = 32768  # tokens of the oracle sample
     sample = (W.to_oracle(k[:ns]), W.to_oracle(v[:ns]))
     del k, v
     g = torch.Generator(device=dev)

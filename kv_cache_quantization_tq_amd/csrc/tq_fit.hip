@@ -41,6 +41,7 @@ struct FitWork {
     unsigned int part_cnt[kMaxLevels][kFitBlocks];
     unsigned int part_max[kFitBlocks];                   // largest |x| bits per block
     int shift;                                           // s, or -1 when the samples cannot be fitted
+    int emax;                                            // |x| < 2^emax for every sample
 };
 
 // largest |x| of a block's samples as the bit pattern of a non-negative
@@ -97,7 +98,12 @@ __global__ void __launch_bounds__(kFitThreads) fit_init_kernel(FitWork *w, int b
         if (threadIdx.x < h) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + h]);
         __syncthreads();
     }
-    if (threadIdx.x == 0) w->shift = fit_shift(red[0], n);
+    if (threadIdx.x == 0) {
+        w->shift = fit_shift(red[0], n);
+        int e = 0;
+        if (red[0] != 0 && red[0] < 0x7f800000u) frexpf(__uint_as_float(red[0]), &e);
+        w->emax = e;
+    }
 }
 
 // Assignment and per-level integer sums of one pass. The block computes the
@@ -159,6 +165,59 @@ template <bool MAGIC> __device__ __forceinline__ long long fixed_point(float x, 
     }
 }
 
+// Bin lookup on a uniform grid (the codec's value-bin method, with a table
+// built by each block from the current boundaries). Cells have width
+// W = 2^(emax - 6) and cover (-2^emax, 2^emax), where every sample lies:
+// cell c = round(x / W + 64) is the low bits of one fma with 2^23 added
+// (x / W is exact, W a power of two). Each cell stores the number of
+// boundaries below its lower edge widened by 1/1024 of a cell and the one
+// boundary inside the widened cell (+inf if none), so base + (x > bnd) is
+// exactly #{j : b_j < x}. If some widened cell holds two boundaries the
+// block uses the binary search instead (every block reaches the same
+// decision: it depends only on the boundaries and emax).
+constexpr int kGridCells = 130;   // c = 0 .. 128, one per thread
+
+struct FitCell {
+    float bnd;
+    unsigned int base;
+};
+
+// number of entries of the ascending array a[0..kMaxLevels) below v (<=
+// v when INCL)
+template <bool INCL> __device__ __forceinline__ int count_below(const float *a, double v)
+{
+    int lo = 0;
+#pragma unroll
+    for (int st = kMaxLevels / 2; st > 0; st >>= 1)
+        if (INCL ? (double)a[lo + st - 1] <= v : (double)a[lo + st - 1] < v) lo += st;
+    return lo;
+}
+
+// Fills lut (one cell per thread) and returns, to every thread, whether
+// every widened cell holds at most one boundary.
+__device__ bool build_grid(const float *bnd, int emax, FitCell *lut)
+{
+    bool bad = emax > 100 || emax < -100;  // keep 2^-(emax-6) and the cell edges in range
+    const int c = threadIdx.x;
+    if (!bad && c < kGridCells) {
+        const double W = ldexp(1.0, emax - 6), LO = -ldexp(1.0, emax);
+        constexpr double margin = 1.0 / 1024.0;
+        const double lo = LO + ((double)c - 0.5 - margin) * W, hi = LO + ((double)c + 0.5 + margin) * W;
+        const int below = count_below<false>(bnd, lo), upto = count_below<true>(bnd, hi);
+        bad = upto - below > 1;
+        lut[c].base = (unsigned int)below;
+        lut[c].bnd = upto > below ? bnd[below] : INFINITY;
+    }
+    return __syncthreads_or(bad) == 0;
+}
+
+__device__ __forceinline__ int grid_bin(float v, float a, float cmag, const FitCell *lut)
+{
+    const float t = __builtin_fmaf(v, a, cmag);
+    const FitCell e = lut[__builtin_bit_cast(unsigned int, t) - 0x4B000000u];
+    return (int)e.base + (v > e.bnd ? 1 : 0);
+}
+
 template <int NS, bool MAGIC>
 __global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x, int64_t n, int levels, FitWork *w)
 {
@@ -176,6 +235,10 @@ __global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x,
         hcnt[j] = 0;
     }
     __syncthreads();
+    __shared__ FitCell lut[kGridCells];
+    const int emax = w->emax;
+    const bool grid = build_grid(bnd, emax, lut);
+    const float ga = ldexpf(1.0f, 6 - emax), gc = 64.0f + 8388608.0f;
     float rb[(1 << RS) - 1];
 #pragma unroll
     for (int t = 0; t < RS; ++t)
@@ -186,8 +249,13 @@ __global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x,
     // the samples are 16-byte aligned), so that their searches overlap
     auto add4 = [&](const float (&v)[4], int valid) {
         int k[4];
+        if (grid) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) k[u] = search_bins<NS, RS>(v[u], bnd, rb);
+            for (int u = 0; u < 4; ++u) k[u] = grid_bin(v[u], ga, gc, lut);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) k[u] = search_bins<NS, RS>(v[u], bnd, rb);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (u < valid) {

@@ -380,13 +380,14 @@ def setup_batch_merge(torch, tq, W, dev):
 
 
 def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
-    """One full fit per step; an iteration reads every sample once."""
+    """One full fit per step: the samples are sorted once, then every
+    iteration searches the sorted keys."""
     n, levels = 1 << 24, 16
     g = torch.Generator(device=dev)
     g.manual_seed(6)
     x = torch.randn(n, generator=g, device=dev, dtype=torch.float32)
     init = tq.lloyd_max_table(4)[0].astype("float64")
-    ws = torch.empty(int(tq.lib().tq_lloyd_max_workspace_bytes()), dtype=torch.uint8, device=dev)
+    ws = torch.empty(int(tq.lib().tq_lloyd_max_workspace_bytes(n)), dtype=torch.uint8, device=dev)
     log(f"workload lloyd_fit: {n} samples, {levels} levels, {iterations} iterations per step")
 
     def step(i, ev=None):
@@ -407,8 +408,13 @@ def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
                 "sample": f"{it} iterations on the first {ns} samples, one thread (numpy)"}
 
     config = {"workload": DESCRIPTION["lloyd_fit"], "samples": n, "levels": levels, "iterations": iterations}
-    # per step: `iterations` passes over the samples (4 bytes each)
-    return step, 1, {"fit": (0, 1, 4 * n * iterations)}, (lambda i: n * iterations), cpu, config
+    # Bytes the sorted method moves per fit: the samples read once for their
+    # largest magnitude (4n), four radix passes each reading and writing the
+    # 4-byte keys (32n), and the prefix pass reading the keys and writing the
+    # int64 prefix sums (12n). The iterations read a few windows of keys and
+    # sums per boundary each and are bound by their dependent latency, not by
+    # bandwidth.
+    return step, 1, {"fit": (0, 1, 48 * n)}, (lambda i: n * iterations), cpu, config
 
 
 def setup_attn_decode(torch, tq, W, dev):

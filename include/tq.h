@@ -249,22 +249,27 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
  * iterative Lloyd-Max fit to unit-normal samples, 500 iterations).
  * --------------------------------------------------------------------- */
 
-/* Bytes of device workspace tq_lloyd_max_fit needs (host only). */
-int64_t tq_lloyd_max_workspace_bytes(void);
+/* Bytes of device workspace tq_lloyd_max_fit needs for n samples (host
+ * only; 16 * n plus about 1.3 KB per 4096 samples). Returns -TQ_E_SHAPE
+ * when n is outside 1 .. 2^31 - 1. */
+int64_t tq_lloyd_max_workspace_bytes(int64_t n);
 
-/* Fit `levels` (2..256) reconstruction levels to n samples (device
- * float32, finite, 4-byte aligned) by `iterations` Lloyd iterations
- * starting from init (host, `levels` strictly ascending binary64 values).
+/* Fit `levels` (2..256) reconstruction levels to n (1 .. 2^31 - 1)
+ * samples (device float32, finite, 4-byte aligned) by `iterations` Lloyd
+ * iterations starting from init (host, `levels` strictly ascending
+ * binary64 values).
  * One iteration: boundaries b_j = (c_j + c_{j+1}) / 2; each sample goes to
  * level k = #{j : b_j < x} (ties to the lower level, the codec's bin
  * rule); c_k = mean of its samples (a level with none keeps its value).
  * Samples are summed as exact integers rint(x * 2^s) with s = min(40, 62 -
  * bitlen(n) - e), |x| < 2^e for every sample, so the result does not depend
- * on summation order: c_k = double(sum_k) * 2^-s / count_k.
+ * on summation order: c_k = double(sum_k) * 2^-s / count_k. The samples
+ * are sorted once in the workspace, so an iteration costs a search per
+ * boundary rather than a pass over the samples.
  * Writes the final centroids (levels) and boundaries (levels - 1, if not
  * NULL) to host memory and waits for the stream before returning.
  * `workspace` is caller-owned device memory of at least
- * tq_lloyd_max_workspace_bytes(), 8-byte aligned; calls sharing a
+ * tq_lloyd_max_workspace_bytes(n), 8-byte aligned; calls sharing a
  * workspace must not overlap. Returns TQ_E_SHAPE if a sample is not finite
  * or magnitudes are too large for the integer sums (s < 0). */
 int32_t tq_lloyd_max_fit(const float *samples, int64_t n, int32_t levels, const double *init, int32_t iterations,

@@ -88,7 +88,7 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
             "tq_filter_rows": (i32, [ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
                                      ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
-            "tq_lloyd_max_workspace_bytes": (i64, []),
+            "tq_lloyd_max_workspace_bytes": (i64, [i64]),
             "tq_attention_workspace_bytes": (i64, [i32, i32, i32, i32, i64]),
             "tq_attention_decode": (i32, [P, i32, ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
                                           ctypes.POINTER(TQConfig), ctypes.c_float, P, i32, P, i64, P]),
@@ -361,7 +361,9 @@ def lloyd_max_fit(samples, levels: int, init, iterations: int = 500, workspace=N
     init_a = np.ascontiguousarray(np.asarray(init, dtype=np.float64))
     if init_a.size != levels:
         raise ValueError("init must hold `levels` values")
-    nbytes = int(lib().tq_lloyd_max_workspace_bytes())
+    nbytes = int(lib().tq_lloyd_max_workspace_bytes(samples.numel()))
+    if nbytes < 0:
+        raise TQError(-nbytes, f"lloyd_max_fit: {samples.numel()} samples")
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=samples.device)
     c = np.zeros(levels, np.float64)

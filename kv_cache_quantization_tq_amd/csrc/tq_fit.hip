@@ -9,16 +9,24 @@
 //                                          the lower level)
 //   centroids   c_k = mean of the samples with k(x) = k    (a level with no
 //                                          sample keeps its centroid)
-// This file runs the iterations on the device with no host round trip (per
-// iteration an assignment launch writing per-block partial sums and an
-// update launch with one block per level).
 //
-// Determinism: each sample enters the per-level sums as the exact integer
+// Method. k(x) depends only on the multiset of boundaries: with them in
+// ascending order b'_0 <= b'_1 <= ..., level k holds exactly the samples in
+// (b'_{k-1}, b'_k]. An iteration therefore needs, per boundary, only the
+// number of samples at or below it and their sum. The samples are sorted
+// once (a least-significant-digit radix sort of a 32-bit key whose order is
+// the order of the values) and their fixed-point values prefix-summed in
+// that order; every iteration then locates each boundary in the sorted keys
+// (a splitter table in LDS, then one segment of keys) and reads counts and
+// sums as differences of positions and prefix sums. All iterations run in
+// one launch of a single block; the samples are read five times in all,
+// not once per iteration.
+//
+// Determinism: each sample enters the sums as the exact integer
 // rint(x * 2^s), with s chosen from the sample count and the largest
-// magnitude so that no sum can overflow 63 bits; integer addition does not
-// depend on order, so the result is the same for any grid and equals a
-// sequential evaluation of the same rule (the centroid is then
-// double(sum) * 2^-s / count in binary64).
+// magnitude so that no partial sum can overflow 63 bits; integer sums do
+// not depend on order, so the centroids equal a sequential evaluation of
+// the same rule (the centroid is double(sum) * 2^-s / count in binary64).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -29,125 +37,74 @@
 namespace {
 
 constexpr int kMaxLevels = 256;
-constexpr int kFitThreads = 256;
-constexpr int kFitBlocks = 1024; // most blocks of a pass (per-block partials below)
+constexpr int kThreads = 256;                // block size of the set-up kernels
+constexpr int kMaxBlocks = 1024;             // most blocks of the magnitude pass
+constexpr int kItems = 16;                   // keys per thread of a sort tile
+constexpr int kTile = kThreads * kItems;     // keys per sort tile
+constexpr int kDigits = 256;                 // 8-bit digits, four passes
+constexpr int kIterThreads = 1024;           // the iteration kernel's block
+constexpr int kSplit = 32768;                // splitter keys held in LDS (128 KB)
+constexpr int kSegMax = 512;                 // keys one wavefront counts in one round
+constexpr int64_t kMaxSamples = ((int64_t)1 << 31) - 1;
 
-// Device workspace (caller-owned). Each pass writes one partial result per
-// block (no contended atomics: a handful of addresses hit by every block
-// of every XCD would serialise), reduced by the next step.
-struct FitWork {
+// Start of the caller's workspace; the sample-sized arrays follow it (see
+// fit_layout).
+struct FitHead {
     double cent[kMaxLevels];
-    unsigned long long part_sum[kMaxLevels][kFitBlocks]; // two's complement int64, level-major
-    unsigned int part_cnt[kMaxLevels][kFitBlocks];
-    unsigned int part_max[kFitBlocks];                   // largest |x| bits per block
-    int shift;                                           // s, or -1 when the samples cannot be fitted
-    int emax;                                            // |x| < 2^emax for every sample
+    unsigned int part_max[kMaxBlocks];  // largest |x| bits per block of the magnitude pass
+    unsigned int digit_total[kDigits];  // keys per digit in the current sort pass
+    int shift;                          // s, or -1 when the samples cannot be fitted
 };
 
-// largest |x| of a block's samples as the bit pattern of a non-negative
-// float (its integer order is the float order; NaN patterns order above
-// +inf)
-__global__ void __launch_bounds__(kFitThreads) fit_absmax_kernel(const float *x, int64_t n, FitWork *w)
+struct FitLayout {
+    int64_t keys_a, keys_b, prefix, hist, tile_sum, total; // byte offsets; total = size
+};
+
+constexpr int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
+// keys_a, keys_b: n sort keys each; prefix: n + 1 prefix sums (int64);
+// hist: per-digit, per-tile key counts; tile_sum: per-tile sums (int64)
+FitLayout fit_layout(int64_t n)
 {
-    unsigned int m = 0;
-    const int64_t tid = (int64_t)blockIdx.x * kFitThreads + threadIdx.x, nt = (int64_t)gridDim.x * kFitThreads;
-    if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-        // whole 16-byte vectors, then the last n % 4 samples
-        const float4 *x4 = reinterpret_cast<const float4 *>(x);
-        for (int64_t v = tid; v < n / 4; v += nt) {
-            const float4 a = x4[v];
-            m = max(max(m, __float_as_uint(a.x) & 0x7fffffffu), __float_as_uint(a.y) & 0x7fffffffu);
-            m = max(max(m, __float_as_uint(a.z) & 0x7fffffffu), __float_as_uint(a.w) & 0x7fffffffu);
-        }
-        if (tid < n % 4) m = max(m, __float_as_uint(x[n / 4 * 4 + tid]) & 0x7fffffffu);
-    } else {
-        for (int64_t i = tid; i < n; i += nt) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
-    }
-    for (int o = 32; o > 0; o >>= 1) m = max(m, (unsigned int)__shfl_xor((int)m, o));
-    __shared__ unsigned int wm[kFitThreads / 64];
-    if ((threadIdx.x & 63) == 0) wm[threadIdx.x / 64] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int i = 1; i < kFitThreads / 64; ++i) m = max(m, wm[i]);
-        w->part_max[blockIdx.x] = m;
-    }
+    const int64_t tiles = (n + kTile - 1) / kTile;
+    FitLayout l;
+    int64_t o = align256((int64_t)sizeof(FitHead));
+    l.keys_a = o;
+    o = align256(o + 4 * n);
+    l.keys_b = o;
+    o = align256(o + 4 * n);
+    l.prefix = o;
+    o = align256(o + 8 * (n + 1));
+    l.hist = o;
+    o = align256(o + 4 * (int64_t)kDigits * tiles);
+    l.tile_sum = o;
+    o = align256(o + 8 * tiles);
+    l.total = o;
+    return l;
 }
 
-// s = min(40, 62 - bitlen(n) - e) with |x| < 2^e for every sample: every
-// |rint(x * 2^s)| <= 2^(62 - bitlen(n)) and n of them sum below 2^62
-__device__ int fit_shift(unsigned int absmax_bits, int64_t n)
+// ---------------------------------------------------------------------------
+// Keys and fixed-point values
+// ---------------------------------------------------------------------------
+
+// A 32-bit key per float whose unsigned order is the order of the values
+// (for finite values; -0 sorts just below +0), and its inverse.
+__device__ __forceinline__ unsigned int float_key(float x)
 {
-    if (absmax_bits >= 0x7f800000u) return -1; // inf or NaN
-    int e = 0;
-    if (absmax_bits != 0) frexpf(__uint_as_float(absmax_bits), &e); // |x| < 2^e
-    int bl = 0;
-    for (uint64_t v = (uint64_t)n; v != 0; v >>= 1) ++bl;
-    int s = 62 - bl - e;
-    return s > 40 ? 40 : s;
+    const unsigned int u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// one block: the largest magnitude over the absmax blocks, then the shift
-__global__ void __launch_bounds__(kFitThreads) fit_init_kernel(FitWork *w, int blocks, int64_t n)
+__device__ __forceinline__ float key_float(unsigned int k)
 {
-    __shared__ unsigned int red[kFitThreads];
-    unsigned int m = 0;
-    for (int b = threadIdx.x; b < blocks; b += kFitThreads) m = max(m, w->part_max[b]);
-    red[threadIdx.x] = m;
-    __syncthreads();
-    for (int h = kFitThreads / 2; h > 0; h >>= 1) {
-        if (threadIdx.x < h) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + h]);
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        w->shift = fit_shift(red[0], n);
-        int e = 0;
-        if (red[0] != 0 && red[0] < 0x7f800000u) frexpf(__uint_as_float(red[0]), &e);
-        w->emax = e;
-    }
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Assignment and per-level integer sums of one pass. The block computes the
-// boundaries from the current centroids, keeps R replicas of the L-level
-// histogram in LDS (R = the largest power of two <= 64 with R * L <=
-// kHistEntries), lane l of every wavefront adding into replica l % R so
-// that lanes of one wavefront rarely contend for an address, folds the
-// replicas pairwise and writes the block's totals as its partial. The
-// search compares the float32 sample with each boundary rounded down to
-// float32, which decides b < x exactly (no float32 lies strictly between a
-// binary64 value and its round-down).
-constexpr int kHistEntries = 1024;
-
-__host__ __device__ inline int fit_replicas(int levels)
+// Key of the last value equal to b: x <= b exactly when float_key(x) <=
+// bound_key(b) (both zeros are <= a zero boundary).
+__device__ __forceinline__ unsigned int bound_key(float b)
 {
-    int r = 64;
-    while (r > 1 && r * levels > kHistEntries) r >>= 1;
-    return r;
-}
-
-// Number of boundaries below v (levels <= 2^NS; bnd padded with +inf):
-// a binary search of NS steps, step t comparing with boundary k + 2^(NS-1-t)
-// - 1. The first RS steps select their boundary from registers (rb holds
-// the 2^RS - 1 boundaries they can need, rb[2^t - 1 + j] for step t and
-// j = k >> (NS - t)); later steps read LDS.
-template <int NS, int RS>
-__device__ __forceinline__ int search_bins(float v, const float *bnd, const float (&rb)[(1 << RS) - 1])
-{
-    int k = 0;
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
-        const int st = 1 << (NS - 1 - t);
-        float bb;
-        if (t < RS) {
-            const int j = k >> (NS - t);
-            bb = rb[(1 << t) - 1];
-#pragma unroll
-            for (int c = 1; c < (1 << t); ++c) bb = j == c ? rb[(1 << t) - 1 + c] : bb;
-        } else {
-            bb = bnd[k + st - 1];
-        }
-        k += bb < v ? st : 0;
-    }
-    return k;
+    return b == 0.0f ? 0x80000000u : float_key(b);
 }
 
 // rint(x * 2^s) as an int64. With MAGIC (every |x * 2^s| < 2^51, which the
@@ -165,195 +122,512 @@ template <bool MAGIC> __device__ __forceinline__ long long fixed_point(float x, 
     }
 }
 
-// Bin lookup on a uniform grid (the codec's value-bin method, with a table
-// built by each block from the current boundaries). Cells have width
-// W = 2^(emax - 6) and cover (-2^emax, 2^emax), where every sample lies:
-// cell c = round(x / W + 64) is the low bits of one fma with 2^23 added
-// (x / W is exact, W a power of two). Each cell stores the number of
-// boundaries below its lower edge widened by 1/1024 of a cell and the one
-// boundary inside the widened cell (+inf if none), so base + (x > bnd) is
-// exactly #{j : b_j < x}. If some widened cell holds two boundaries the
-// block uses the binary search instead (every block reaches the same
-// decision: it depends only on the boundaries and emax).
-constexpr int kGridCells = 130;   // c = 0 .. 128, one per thread
+// ---------------------------------------------------------------------------
+// Block and wavefront helpers (kThreads threads)
+// ---------------------------------------------------------------------------
 
-struct FitCell {
-    float bnd;
-    unsigned int base;
-};
-
-// number of entries of the ascending array a[0..kMaxLevels) below v (<=
-// v when INCL)
-template <bool INCL> __device__ __forceinline__ int count_below(const float *a, double v)
+__device__ __forceinline__ unsigned long long lanes_below()
 {
-    int lo = 0;
+    return (1ull << (threadIdx.x & 63)) - 1ull;
+}
+
+// Exclusive prefix of v over the block's threads in thread order; `total`
+// receives the sum over all threads.
+template <typename T> __device__ T block_exclusive_scan(T v, T &total)
+{
+    __shared__ T wsum[kThreads / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    T x = v;
 #pragma unroll
-    for (int st = kMaxLevels / 2; st > 0; st >>= 1)
-        if (INCL ? (double)a[lo + st - 1] <= v : (double)a[lo + st - 1] < v) lo += st;
-    return lo;
-}
-
-// Fills lut (one cell per thread) and returns, to every thread, whether
-// every widened cell holds at most one boundary.
-__device__ bool build_grid(const float *bnd, int emax, FitCell *lut)
-{
-    bool bad = emax > 100 || emax < -100;  // keep 2^-(emax-6) and the cell edges in range
-    const int c = threadIdx.x;
-    if (!bad && c < kGridCells) {
-        const double W = ldexp(1.0, emax - 6), LO = -ldexp(1.0, emax);
-        constexpr double margin = 1.0 / 1024.0;
-        const double lo = LO + ((double)c - 0.5 - margin) * W, hi = LO + ((double)c + 0.5 + margin) * W;
-        const int below = count_below<false>(bnd, lo), upto = count_below<true>(bnd, hi);
-        bad = upto - below > 1;
-        lut[c].base = (unsigned int)below;
-        lut[c].bnd = upto > below ? bnd[below] : INFINITY;
+    for (int o = 1; o < 64; o <<= 1) {
+        const T y = __shfl_up(x, o);
+        if (lane >= o) x += y;
     }
-    return __syncthreads_or(bad) == 0;
-}
-
-__device__ __forceinline__ int grid_bin(float v, float a, float cmag, const FitCell *lut)
-{
-    const float t = __builtin_fmaf(v, a, cmag);
-    const FitCell e = lut[__builtin_bit_cast(unsigned int, t) - 0x4B000000u];
-    return (int)e.base + (v > e.bnd ? 1 : 0);
-}
-
-template <int NS, bool MAGIC>
-__global__ void __launch_bounds__(kFitThreads) fit_assign_kernel(const float *x, int64_t n, int levels, FitWork *w)
-{
-    constexpr int RS = NS < 2 ? NS : 2;
-    __shared__ float bnd[kMaxLevels];
-    __shared__ unsigned long long hsum[kHistEntries];
-    __shared__ unsigned int hcnt[kHistEntries];
-    const int s = w->shift;
-    if (s < 0) return;
-    const int R = fit_replicas(levels);
-    for (int j = threadIdx.x; j < kMaxLevels; j += kFitThreads)
-        bnd[j] = j < levels - 1 ? __double2float_rd((w->cent[j] + w->cent[j + 1]) * 0.5) : INFINITY;
-    for (int j = threadIdx.x; j < levels * R; j += kFitThreads) {
-        hsum[j] = 0;
-        hcnt[j] = 0;
-    }
+    if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    __shared__ FitCell lut[kGridCells];
-    const int emax = w->emax;
-    const bool grid = build_grid(bnd, emax, lut);
-    const float ga = ldexpf(1.0f, 6 - emax), gc = 64.0f + 8388608.0f;
-    float rb[(1 << RS) - 1];
+    T base = 0, tot = 0;
 #pragma unroll
-    for (int t = 0; t < RS; ++t)
+    for (int w = 0; w < kThreads / 64; ++w) {
+        base += w < wave ? wsum[w] : (T)0;
+        tot += wsum[w];
+    }
+    __syncthreads(); // wsum is reused by the next call
+    total = tot;
+    return base + x - v;
+}
+
+// Lanes of the wavefront, among those with `valid`, whose digit equals this
+// lane's (eight votes, one per digit bit).
+__device__ __forceinline__ unsigned long long match_digit(unsigned int d, bool valid)
+{
+    unsigned long long m = __ballot(valid);
 #pragma unroll
-        for (int j = 0; j < (1 << t); ++j) rb[(1 << t) - 1 + j] = bnd[(2 * j + 1) * (1 << (NS - 1 - t)) - 1];
-    const int rep = (threadIdx.x & 63) % R;
-    // four samples at a time (one 16-byte vector per thread and step when
-    // the samples are 16-byte aligned), so that their searches overlap
-    auto add4 = [&](const float (&v)[4], int valid) {
-        int k[4];
-        if (grid) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) k[u] = grid_bin(v[u], ga, gc, lut);
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) k[u] = search_bins<NS, RS>(v[u], bnd, rb);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (u < valid) {
-                const long long q = fixed_point<MAGIC>(v[u], s);
-                atomicAdd(&hsum[k[u] * R + rep], (unsigned long long)q);
-                atomicAdd(&hcnt[k[u] * R + rep], 1u);
-            }
-        }
-    };
-    const int64_t tid = (int64_t)blockIdx.x * kFitThreads + threadIdx.x, nt = (int64_t)gridDim.x * kFitThreads;
+    for (int b = 0; b < 8; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const unsigned long long v = __ballot(bit);
+        m &= bit ? v : ~v;
+    }
+    return m;
+}
+
+// ---------------------------------------------------------------------------
+// Largest magnitude and the fixed-point shift
+// ---------------------------------------------------------------------------
+
+// largest |x| of a block's samples as the bit pattern of a non-negative
+// float (its integer order is the float order; NaN patterns order above
+// +inf)
+__global__ void __launch_bounds__(kThreads) fit_absmax_kernel(const float *x, int64_t n, FitHead *h)
+{
+    unsigned int m = 0;
+    const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x, nt = (int64_t)gridDim.x * kThreads;
     if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+        // whole 16-byte vectors, then the last n % 4 samples
         const float4 *x4 = reinterpret_cast<const float4 *>(x);
-        for (int64_t vi = tid; vi < n / 4; vi += nt) {
-            const float4 a = x4[vi];
-            const float v[4] = {a.x, a.y, a.z, a.w};
-            add4(v, 4);
+        for (int64_t v = tid; v < n / 4; v += nt) {
+            const float4 a = x4[v];
+            m = max(max(m, __float_as_uint(a.x) & 0x7fffffffu), __float_as_uint(a.y) & 0x7fffffffu);
+            m = max(max(m, __float_as_uint(a.z) & 0x7fffffffu), __float_as_uint(a.w) & 0x7fffffffu);
         }
-        if (tid == 0 && n % 4 != 0) {
-            float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            for (int u = 0; u < (int)(n % 4); ++u) v[u] = x[n / 4 * 4 + u];
-            add4(v, (int)(n % 4));
-        }
+        if (tid < n % 4) m = max(m, __float_as_uint(x[n / 4 * 4 + tid]) & 0x7fffffffu);
     } else {
-        for (int64_t i0 = tid; i0 < n; i0 += 4 * nt) {
-            float v[4];
-            int valid = 0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t i = i0 + u * nt;
-                v[u] = i < n ? x[i] : 0.0f;
-                valid += i < n ? 1 : 0;
-            }
-            add4(v, valid);
-        }
+        for (int64_t i = tid; i < n; i += nt) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
     }
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (unsigned int)__shfl_xor((int)m, o));
+    __shared__ unsigned int wm[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x / 64] = m;
     __syncthreads();
-    for (int half = R / 2; half > 0; half >>= 1) {
-        for (int j = threadIdx.x; j < levels * half; j += kFitThreads) {
-            const int kk = j / half, r = j % half;
-            hsum[kk * R + r] += hsum[kk * R + r + half];
-            hcnt[kk * R + r] += hcnt[kk * R + r + half];
-        }
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < kThreads / 64; ++i) m = max(m, wm[i]);
+        h->part_max[blockIdx.x] = m;
+    }
+}
+
+// s = min(40, 62 - bitlen(n) - e) with |x| < 2^e for every sample: every
+// |rint(x * 2^s)| <= 2^(62 - bitlen(n)) and n of them sum below 2^62
+__device__ int fit_shift(unsigned int absmax_bits, int64_t n)
+{
+    if (absmax_bits >= 0x7f800000u) return -1; // inf or NaN
+    int e = 0;
+    if (absmax_bits != 0) frexpf(__uint_as_float(absmax_bits), &e); // |x| < 2^e
+    int bl = 0;
+    for (uint64_t v = (uint64_t)n; v != 0; v >>= 1) ++bl;
+    const int s = 62 - bl - e;
+    return s > 40 ? 40 : s;
+}
+
+// one block: the largest magnitude over the magnitude pass's blocks, then
+// the shift
+__global__ void __launch_bounds__(kThreads) fit_init_kernel(FitHead *h, int blocks, int64_t n)
+{
+    __shared__ unsigned int red[kThreads];
+    unsigned int m = 0;
+    for (int b = threadIdx.x; b < blocks; b += kThreads) m = max(m, h->part_max[b]);
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int half = kThreads / 2; half > 0; half >>= 1) {
+        if (threadIdx.x < half) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + half]);
         __syncthreads();
     }
-    for (int kk = threadIdx.x; kk < levels; kk += kFitThreads) {
-        w->part_sum[kk][blockIdx.x] = hsum[kk * R];
-        w->part_cnt[kk][blockIdx.x] = hcnt[kk * R];
+    if (threadIdx.x == 0) h->shift = fit_shift(red[0], n);
+}
+
+// ---------------------------------------------------------------------------
+// Radix sort of the keys: per pass a count, a scan and a stable scatter
+// ---------------------------------------------------------------------------
+// A tile is kTile consecutive keys; thread t holds keys t, t + kThreads,
+// ... of its tile, so step i of a tile covers kThreads consecutive keys in
+// thread order. The first pass reads the samples and forms their keys.
+
+template <bool FROM_SAMPLES> __device__ __forceinline__ unsigned int load_key(const void *src, int64_t i)
+{
+    if constexpr (FROM_SAMPLES) return float_key(static_cast<const float *>(src)[i]);
+    else return static_cast<const unsigned int *>(src)[i];
+}
+
+template <bool FROM_SAMPLES>
+__device__ __forceinline__ void load_tile(const void *src, int64_t n, unsigned int (&key)[kItems])
+{
+    const int64_t t0 = (int64_t)blockIdx.x * kTile + threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int64_t idx = t0 + (int64_t)i * kThreads;
+        key[i] = idx < n ? load_key<FROM_SAMPLES>(src, idx) : 0u;
     }
 }
 
-// one block per level: the level's total over the pass's block partials
-// (contiguous, level-major; each thread loads its few independently), then
-// its new centroid (a level with no sample keeps its value)
-__global__ void __launch_bounds__(kFitThreads) fit_update_kernel(FitWork *w, int blocks)
+// keys of each digit in each tile, digit-major: hist[d * tiles + tile]
+template <bool FROM_SAMPLES>
+__global__ void __launch_bounds__(kThreads)
+fit_digit_count_kernel(const void *src, int64_t n, int sh, unsigned int *hist, int64_t tiles, const FitHead *h)
 {
-    __shared__ unsigned long long rs[kFitThreads / 64][2];
-    const int s = w->shift;
-    if (s < 0) return;
-    const int k = blockIdx.x, tid = threadIdx.x;
-    unsigned long long sm = 0, c = 0;
+    if (h->shift < 0) return;
+    __shared__ unsigned int cnt[kDigits];
+    cnt[threadIdx.x] = 0;
+    unsigned int key[kItems];
+    load_tile<FROM_SAMPLES>(src, n, key);
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * kTile + threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < kFitBlocks / kFitThreads; ++i) {
-        const int b = tid + i * kFitThreads;
-        if (b < blocks) {
-            sm += w->part_sum[k][b];
-            c += w->part_cnt[k][b];
-        }
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-        sm += __shfl_xor(sm, o);
-        c += __shfl_xor(c, o);
-    }
-    if ((tid & 63) == 0) {
-        rs[tid / 64][0] = sm;
-        rs[tid / 64][1] = c;
+    for (int i = 0; i < kItems; ++i) {
+        const bool valid = t0 + (int64_t)i * kThreads < n;
+        const unsigned int d = (key[i] >> sh) & 255u;
+        const unsigned long long peers = match_digit(d, valid);
+        // one LDS add per distinct digit of the wavefront
+        if (valid && (peers & lanes_below()) == 0) atomicAdd(&cnt[d], (unsigned int)__popcll(peers));
     }
     __syncthreads();
-    if (tid == 0) {
-        for (int v = 1; v < kFitThreads / 64; ++v) {
-            sm += rs[v][0];
-            c += rs[v][1];
+    hist[(int64_t)threadIdx.x * tiles + blockIdx.x] = cnt[threadIdx.x];
+}
+
+// one block per digit: the digit's per-tile counts become exclusive
+// prefixes within the digit, and the digit's total goes to the head
+__global__ void __launch_bounds__(kThreads) fit_digit_scan_kernel(unsigned int *hist, int64_t tiles, FitHead *h)
+{
+    if (h->shift < 0) return;
+    unsigned int *row = hist + (int64_t)blockIdx.x * tiles;
+    const int64_t chunk = (tiles + kThreads - 1) / kThreads;
+    const int64_t lo = min((int64_t)threadIdx.x * chunk, tiles), hi = min(lo + chunk, tiles);
+    unsigned int s = 0;
+    for (int64_t j = lo; j < hi; ++j) s += row[j];
+    unsigned int total;
+    unsigned int off = block_exclusive_scan<unsigned int>(s, total);
+    for (int64_t j = lo; j < hi; ++j) {
+        const unsigned int v = row[j];
+        row[j] = off;
+        off += v;
+    }
+    if (threadIdx.x == 0) h->digit_total[blockIdx.x] = total;
+}
+
+// Stable scatter of a tile: a key goes to (keys of smaller digits) + (keys
+// of its digit in earlier tiles) + (keys of its digit earlier in this
+// tile). Within a step the earlier keys of the same digit are those of
+// lower lanes of the same wavefront and of lower wavefronts.
+template <bool FROM_SAMPLES>
+__global__ void __launch_bounds__(kThreads)
+fit_digit_scatter_kernel(const void *src, int64_t n, int sh, const unsigned int *hist, int64_t tiles,
+                         const FitHead *h, unsigned int *dst)
+{
+    if (h->shift < 0) return;
+    __shared__ unsigned int start[kDigits];
+    __shared__ unsigned int wcnt[kThreads / 64][kDigits];
+    const int t = threadIdx.x, wave = t >> 6;
+    unsigned int total;
+    const unsigned int base = block_exclusive_scan<unsigned int>(h->digit_total[t], total);
+    start[t] = base + hist[(int64_t)t * tiles + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) wcnt[w][t] = 0;
+    unsigned int key[kItems];
+    load_tile<FROM_SAMPLES>(src, n, key);
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * kTile + t;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const bool valid = t0 + (int64_t)i * kThreads < n;
+        const unsigned int d = (key[i] >> sh) & 255u;
+        const unsigned long long peers = match_digit(d, valid);
+        const unsigned int rank = (unsigned int)__popcll(peers & lanes_below());
+        if (valid && rank == 0) wcnt[wave][d] = (unsigned int)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            unsigned int p = start[d] + rank;
+            for (int w = 0; w < wave; ++w) p += wcnt[w][d];
+            dst[p] = key[i];
         }
-        if (c != 0) w->cent[k] = ldexp((double)(long long)sm, -s) / (double)c;
+        __syncthreads();
+        unsigned int step = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            step += wcnt[w][t];
+            wcnt[w][t] = 0;
+        }
+        start[t] += step;
+        __syncthreads();
     }
 }
 
-template <bool MAGIC> const void *assign_kernel(int ns)
+// ---------------------------------------------------------------------------
+// Prefix sums of the fixed-point values in sorted order
+// ---------------------------------------------------------------------------
+
+// sum of each tile's fixed-point values
+template <bool MAGIC>
+__global__ void __launch_bounds__(kThreads)
+fit_tile_sum_kernel(const unsigned int *keys, int64_t n, const FitHead *h, long long *tile_sum)
 {
-    switch (ns) {
-    case 1: return reinterpret_cast<const void *>(&fit_assign_kernel<1, MAGIC>);
-    case 2: return reinterpret_cast<const void *>(&fit_assign_kernel<2, MAGIC>);
-    case 3: return reinterpret_cast<const void *>(&fit_assign_kernel<3, MAGIC>);
-    case 4: return reinterpret_cast<const void *>(&fit_assign_kernel<4, MAGIC>);
-    case 5: return reinterpret_cast<const void *>(&fit_assign_kernel<5, MAGIC>);
-    case 6: return reinterpret_cast<const void *>(&fit_assign_kernel<6, MAGIC>);
-    case 7: return reinterpret_cast<const void *>(&fit_assign_kernel<7, MAGIC>);
-    default: return reinterpret_cast<const void *>(&fit_assign_kernel<8, MAGIC>);
+    const int s = h->shift;
+    if (s < 0) return;
+    const int64_t t0 = (int64_t)blockIdx.x * kTile + threadIdx.x;
+    long long acc = 0;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int64_t idx = t0 + (int64_t)i * kThreads;
+        if (idx < n) acc += fixed_point<MAGIC>(key_float(keys[idx]), s);
     }
+    long long total;
+    block_exclusive_scan<long long>(acc, total);
+    if (threadIdx.x == 0) tile_sum[blockIdx.x] = total;
+}
+
+// one block: the tile sums become exclusive prefixes
+__global__ void __launch_bounds__(kThreads) fit_tile_scan_kernel(long long *tile_sum, int64_t tiles, const FitHead *h)
+{
+    if (h->shift < 0) return;
+    const int64_t chunk = (tiles + kThreads - 1) / kThreads;
+    const int64_t lo = min((int64_t)threadIdx.x * chunk, tiles), hi = min(lo + chunk, tiles);
+    long long s = 0;
+    for (int64_t j = lo; j < hi; ++j) s += tile_sum[j];
+    long long total;
+    long long off = block_exclusive_scan<long long>(s, total);
+    for (int64_t j = lo; j < hi; ++j) {
+        const long long v = tile_sum[j];
+        tile_sum[j] = off;
+        off += v;
+    }
+}
+
+// prefix[i] = sum of the fixed-point values of sorted keys 0 .. i-1. A tile
+// is staged in LDS (one padding entry per 16, so that each thread's run of
+// 16 consecutive entries falls in distinct banks), each thread sums a run,
+// and the block scan of the runs gives every prefix.
+template <bool MAGIC>
+__global__ void __launch_bounds__(kThreads)
+fit_prefix_kernel(const unsigned int *keys, int64_t n, const FitHead *h, const long long *tile_sum, long long *prefix)
+{
+    const int s = h->shift;
+    if (s < 0) return;
+    __shared__ long long q[kTile + kTile / kItems];
+    auto slot = [](int j) { return j + (j >> 4); };
+    const int t = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kTile;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int j = i * kThreads + t;
+        q[slot(j)] = t0 + j < n ? fixed_point<MAGIC>(key_float(keys[t0 + j]), s) : 0;
+    }
+    __syncthreads();
+    long long run = 0;
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) run += q[slot(t * kItems + k)];
+    long long total;
+    long long acc = block_exclusive_scan<long long>(run, total) + tile_sum[blockIdx.x];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        acc += q[slot(t * kItems + k)];
+        q[slot(t * kItems + k)] = acc; // inclusive prefix of entry t * kItems + k
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int j = i * kThreads + t;
+        if (t0 + j < n) prefix[t0 + j + 1] = q[slot(j)];
+    }
+    if (blockIdx.x == 0 && t == 0) prefix[0] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// The iterations
+// ---------------------------------------------------------------------------
+
+// The last window of sorted keys a wavefront counted for one boundary:
+// keys[glo .. glo + glen) (glen <= kSegMax) with keys[glo] <= K and the
+// first key above K in (glo, glo + glen]. Lane l holds keys glo + 64 e + l
+// and the prefix sums at those positions; the window is reused while it
+// still brackets the boundary (boundaries move little between late
+// iterations), which costs no memory access at all.
+struct Window {
+    int64_t glo;
+    int glen;
+    unsigned int first;  // keys[glo]
+    unsigned int next;   // keys[glo + glen], or 0xffffffff (above every key) at the end
+    bool ok;
+    unsigned int kv[kSegMax / 64];   // 0xffffffff past the window
+    long long pv[kSegMax / 64 + 1];  // prefix[glo + 64 e + l] for 64 e + l <= glen
+};
+
+// Position of boundary key K in the sorted keys (the number of keys <= K)
+// and the prefix sum there, computed by one wavefront (K is uniform).
+// spl[i] = keys[i * seg] for i < nsp. Each narrowing round probes 64
+// evenly spaced candidates and keeps the interval after the last one <= K.
+__device__ __forceinline__ void locate(const unsigned int *__restrict__ keys, const long long *__restrict__ prefix, int64_t n,
+                       int64_t seg, int nsp, const unsigned int *spl, unsigned int K, Window &w, int64_t &pos,
+                       long long &psum)
+{
+    constexpr int R = kSegMax / 64;
+    const int lane = threadIdx.x & 63;
+    if (!(w.ok && w.first <= K && K < w.next)) {
+        // last splitter <= K, in LDS
+        int lo = 0, len = nsp;
+        bool none = false;
+        while (len > 64) {
+            const int stride = (len + 63) / 64;
+            const int i = lo + lane * stride;
+            const int c = __popcll(__ballot(i < lo + len && spl[i] <= K));
+            if (c == 0) { // only possible in the first round (spl[lo] <= K after it)
+                none = true;
+                break;
+            }
+            lo += (c - 1) * stride;
+            len = min(stride, len - (c - 1) * stride);
+        }
+        if (!none) {
+            const int c = __popcll(__ballot(lane < len && spl[lo + lane] <= K));
+            none = c == 0;
+            lo += c - 1;
+        }
+        if (none) { // every key is above K
+            w.ok = false;
+            pos = 0;
+            psum = 0;
+            return;
+        }
+        // keys[glo] <= K, and the first key above K is in (glo, glo + glen]
+        int64_t glo = (int64_t)lo * seg, glen = min(seg, n - glo);
+        while (glen > kSegMax) {
+            const int64_t stride = (glen + 63) / 64;
+            const int64_t i = glo + lane * stride;
+            const int c = __popcll(__ballot(i < glo + glen && keys[i] <= K));
+            glo += (c - 1) * stride;
+            glen = min(stride, glen - (c - 1) * stride);
+        }
+        // the window's keys and the prefix sums at every candidate position,
+        // in one round of loads
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            const int j = e * 64 + lane;
+            w.kv[e] = j < glen ? keys[glo + j] : 0xffffffffu;
+            w.pv[e] = j <= glen ? prefix[glo + j] : 0;
+        }
+        w.pv[R] = lane == 0 && R * 64 <= glen ? prefix[glo + R * 64] : 0;
+        w.next = glo + glen < n ? keys[glo + glen] : 0xffffffffu;
+        w.first = (unsigned int)__shfl((int)w.kv[0], 0);
+        w.glo = glo;
+        w.glen = (int)glen;
+        w.ok = true;
+    }
+    // the keys <= K are a prefix of the window
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < R; ++e) cnt += __popcll(__ballot(w.kv[e] <= K));
+    long long v = w.pv[0];
+#pragma unroll
+    for (int e = 1; e <= R; ++e) v = (cnt >> 6) == e ? w.pv[e] : v;
+    pos = w.glo + cnt;
+    psum = __shfl(v, cnt & 63);
+}
+
+// All iterations in one block. An iteration: one wavefront per boundary
+// locates it (wavefront w takes boundaries w, w + 16, ...; the windows of
+// the first kCached of them stay in its registers); then thread k forms the
+// new centroids of levels k .. k + 2 from the counts and sums (a level with
+// no sample keeps its value; centroids are double-buffered so that every
+// thread reads the old values) and the key of boundary k for the next
+// iteration, rounded down to float32 (which decides b < x exactly for
+// float32 samples: no float32 lies strictly between a binary64 value and
+// its round-down). Boundaries out of ascending order are sorted.
+constexpr int kCached = 1;
+
+__device__ __forceinline__ unsigned int boundary_key(double lo, double hi)
+{
+    return bound_key(__double2float_rd((lo + hi) * 0.5));
+}
+
+__global__ void __launch_bounds__(kIterThreads)
+fit_iterate_kernel(const unsigned int *__restrict__ keys, const long long *__restrict__ prefix, int64_t n,
+                   int levels, int iterations, FitHead *h)
+{
+    const int s = h->shift;
+    if (s < 0) return;
+    __shared__ unsigned int spl[kSplit];
+    __shared__ double cent[2][kMaxLevels];
+    __shared__ unsigned int bkey[kMaxLevels];
+    __shared__ int64_t pos[kMaxLevels];
+    __shared__ long long psum[kMaxLevels];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    constexpr int kWaves = kIterThreads / 64;
+    const int64_t seg = (n + kSplit - 1) / kSplit;
+    const int nsp = (int)((n + seg - 1) / seg);
+    for (int i = t; i < nsp; i += kIterThreads) spl[i] = keys[(int64_t)i * seg];
+    for (int k = t; k < levels; k += kIterThreads) cent[0][k] = h->cent[k];
+    const long long total = prefix[n];
+    const int nb = levels - 1;
+    __syncthreads();
+    auto sort_keys = [&](bool down) {
+        if (__syncthreads_or(down)) {
+            // ascending order by rank, equal keys by index
+            unsigned int mine = 0;
+            int r = 0;
+            if (t < nb) {
+                mine = bkey[t];
+                for (int j = 0; j < nb; ++j) {
+                    const unsigned int o = bkey[j];
+                    r += (o < mine || (o == mine && j < t)) ? 1 : 0;
+                }
+            }
+            __syncthreads();
+            if (t < nb) bkey[r] = mine;
+            __syncthreads();
+        }
+    };
+    unsigned int k0 = 0, k1 = 0;
+    if (t < nb) k0 = bkey[t] = boundary_key(cent[0][t], cent[0][t + 1]);
+    __syncthreads();
+    if (t + 1 < nb) k1 = bkey[t + 1];
+    sort_keys(t + 1 < nb && k0 > k1);
+    Window win[kCached];
+#pragma unroll
+    for (int m = 0; m < kCached; ++m) win[m].ok = false;
+    int cur = 0;
+    for (int it = 0; it < iterations; ++it) {
+#pragma unroll
+        for (int m = 0; m < kCached; ++m) {
+            const int j = wave + m * kWaves;
+            if (j < nb) {
+                int64_t p;
+                long long ps;
+                locate(keys, prefix, n, seg, nsp, spl, bkey[j], win[m], p, ps);
+                if (lane == 0) {
+                    pos[j] = p;
+                    psum[j] = ps;
+                }
+            }
+        }
+        for (int j = wave + kCached * kWaves; j < nb; j += kWaves) {
+            Window tmp;
+            tmp.ok = false;
+            int64_t p;
+            long long ps;
+            locate(keys, prefix, n, seg, nsp, spl, bkey[j], tmp, p, ps);
+            if (lane == 0) {
+                pos[j] = p;
+                psum[j] = ps;
+            }
+        }
+        __syncthreads();
+        auto newc = [&](int k) {
+            const int64_t hi = k < nb ? pos[k] : n, lo = k > 0 ? pos[k - 1] : 0;
+            const long long shi = k < nb ? psum[k] : total, slo = k > 0 ? psum[k - 1] : 0;
+            return hi > lo ? ldexp((double)(shi - slo), -s) / (double)(hi - lo) : cent[cur][k];
+        };
+        bool down = false;
+        if (t < levels) {
+            const double c0 = newc(t);
+            cent[cur ^ 1][t] = c0;
+            if (t < nb) {
+                const double c1 = newc(t + 1);
+                k0 = boundary_key(c0, c1);
+                if (t + 1 < nb) {
+                    k1 = boundary_key(c1, newc(t + 2));
+                    down = k0 > k1;
+                }
+                bkey[t] = k0; // every wavefront has read bkey before the barrier above
+            }
+        }
+        sort_keys(down);
+        cur ^= 1;
+    }
+    for (int k = t; k < levels; k += kIterThreads) h->cent[k] = cent[cur][k];
 }
 
 int32_t hip_ok(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_HIP; }
@@ -362,50 +636,89 @@ int32_t hip_ok(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_HIP; }
 
 extern "C" {
 
-int64_t tq_lloyd_max_workspace_bytes(void) { return (int64_t)sizeof(FitWork); }
+int64_t tq_lloyd_max_workspace_bytes(int64_t n)
+{
+    if (n < 1 || n > kMaxSamples) return -TQ_E_SHAPE;
+    return fit_layout(n).total;
+}
 
 int32_t tq_lloyd_max_fit(const float *samples, int64_t n, int32_t levels, const double *init, int32_t iterations,
                          double *centroids, double *boundaries, void *workspace, int64_t workspace_bytes,
                          void *stream)
 {
     if (levels < 2 || levels > kMaxLevels) return TQ_E_BITS;
-    if (n < 1 || n > ((int64_t)1 << 40) || iterations < 0) return TQ_E_SHAPE;
+    if (n < 1 || n > kMaxSamples || iterations < 0) return TQ_E_SHAPE;
     if (samples == nullptr || init == nullptr || centroids == nullptr || workspace == nullptr) return TQ_E_NULL;
-    if (workspace_bytes < (int64_t)sizeof(FitWork)) return TQ_E_SHAPE;
+    const FitLayout lay = fit_layout(n);
+    if (workspace_bytes < lay.total) return TQ_E_SHAPE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 7) != 0 || (reinterpret_cast<uintptr_t>(samples) & 3) != 0)
         return TQ_E_ALIGN;
     for (int j = 1; j < levels; ++j)
         if (!(init[j - 1] < init[j])) return TQ_E_SHAPE; // strictly ascending, finite order
     hipStream_t st = (hipStream_t)stream;
-    FitWork *w = static_cast<FitWork *>(workspace);
+    char *ws = static_cast<char *>(workspace);
+    FitHead *h = reinterpret_cast<FitHead *>(ws);
+    unsigned int *keys_a = reinterpret_cast<unsigned int *>(ws + lay.keys_a);
+    unsigned int *keys_b = reinterpret_cast<unsigned int *>(ws + lay.keys_b);
+    long long *prefix = reinterpret_cast<long long *>(ws + lay.prefix);
+    unsigned int *hist = reinterpret_cast<unsigned int *>(ws + lay.hist);
+    long long *tile_sum = reinterpret_cast<long long *>(ws + lay.tile_sum);
     int32_t r = TQ_OK;
-    if ((r = hip_ok(hipMemcpyAsync(w->cent, init, sizeof(double) * levels, hipMemcpyHostToDevice, st))) != TQ_OK)
+    if ((r = hip_ok(hipMemcpyAsync(h->cent, init, sizeof(double) * levels, hipMemcpyHostToDevice, st))) != TQ_OK)
         return r;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                  hipSuccess || cus <= 0)
         cus = 256;
-    const int64_t want = (n / 4 + kFitThreads) / kFitThreads;
-    const int64_t cap = 4LL * cus < kFitBlocks ? 4LL * cus : kFitBlocks;
+    const int64_t want = (n / 4 + kThreads) / kThreads;
+    const int64_t cap = 4LL * cus < kMaxBlocks ? 4LL * cus : kMaxBlocks;
     const int grid = (int)(want < cap ? want : cap);
-    hipLaunchKernelGGL(fit_absmax_kernel, dim3(grid), dim3(kFitThreads), 0, st, samples, n, w);
-    hipLaunchKernelGGL(fit_init_kernel, dim3(1), dim3(kFitThreads), 0, st, w, grid, n);
-    int ns = 1;
-    while ((1 << ns) < levels) ++ns; // levels <= 2^ns
-    const void *assign = n >= (1 << 11) ? assign_kernel<true>(ns) : assign_kernel<false>(ns);
-    int lv = levels;
-    for (int32_t it = 0; it < iterations; ++it) {
-        const float *xs = samples;
-        int64_t nn = n;
-        void *args[] = {&xs, &nn, &lv, &w};
-        if ((r = hip_ok(hipLaunchKernel(assign, dim3(grid), dim3(kFitThreads), args, 0, st))) != TQ_OK) return r;
-        hipLaunchKernelGGL(fit_update_kernel, dim3(levels), dim3(kFitThreads), 0, st, w, grid);
+    hipLaunchKernelGGL(fit_absmax_kernel, dim3(grid), dim3(kThreads), 0, st, samples, n, h);
+    hipLaunchKernelGGL(fit_init_kernel, dim3(1), dim3(kThreads), 0, st, h, grid, n);
+    if (iterations > 0) {
+        const int64_t tiles = (n + kTile - 1) / kTile;
+        // four passes: samples -> b -> a -> b -> a
+        for (int pass = 0; pass < 4; ++pass) {
+            const int sh = 8 * pass;
+            const void *src = pass == 0 ? static_cast<const void *>(samples) : (pass & 1 ? keys_b : keys_a);
+            unsigned int *dst = pass & 1 ? keys_a : keys_b;
+            if (pass == 0) {
+                hipLaunchKernelGGL(fit_digit_count_kernel<true>, dim3(tiles), dim3(kThreads), 0, st, src, n, sh, hist,
+                                   tiles, h);
+            } else {
+                hipLaunchKernelGGL(fit_digit_count_kernel<false>, dim3(tiles), dim3(kThreads), 0, st, src, n, sh, hist,
+                                   tiles, h);
+            }
+            hipLaunchKernelGGL(fit_digit_scan_kernel, dim3(kDigits), dim3(kThreads), 0, st, hist, tiles, h);
+            if (pass == 0) {
+                hipLaunchKernelGGL(fit_digit_scatter_kernel<true>, dim3(tiles), dim3(kThreads), 0, st, src, n, sh,
+                                   hist, tiles, h, dst);
+            } else {
+                hipLaunchKernelGGL(fit_digit_scatter_kernel<false>, dim3(tiles), dim3(kThreads), 0, st, src, n, sh,
+                                   hist, tiles, h, dst);
+            }
+        }
+        if (n >= (1 << 11)) {
+            hipLaunchKernelGGL(fit_tile_sum_kernel<true>, dim3(tiles), dim3(kThreads), 0, st, keys_a, n, h, tile_sum);
+        } else {
+            hipLaunchKernelGGL(fit_tile_sum_kernel<false>, dim3(tiles), dim3(kThreads), 0, st, keys_a, n, h, tile_sum);
+        }
+        hipLaunchKernelGGL(fit_tile_scan_kernel, dim3(1), dim3(kThreads), 0, st, tile_sum, tiles, h);
+        if (n >= (1 << 11)) {
+            hipLaunchKernelGGL(fit_prefix_kernel<true>, dim3(tiles), dim3(kThreads), 0, st, keys_a, n, h, tile_sum,
+                               prefix);
+        } else {
+            hipLaunchKernelGGL(fit_prefix_kernel<false>, dim3(tiles), dim3(kThreads), 0, st, keys_a, n, h, tile_sum,
+                               prefix);
+        }
+        hipLaunchKernelGGL(fit_iterate_kernel, dim3(1), dim3(kIterThreads), 0, st, keys_a, prefix, n, levels,
+                           iterations, h);
     }
     if ((r = hip_ok(hipGetLastError())) != TQ_OK) return r;
     int shift = 0;
-    if ((r = hip_ok(hipMemcpyAsync(centroids, w->cent, sizeof(double) * levels, hipMemcpyDeviceToHost, st))) != TQ_OK)
+    if ((r = hip_ok(hipMemcpyAsync(centroids, h->cent, sizeof(double) * levels, hipMemcpyDeviceToHost, st))) != TQ_OK)
         return r;
-    if ((r = hip_ok(hipMemcpyAsync(&shift, &w->shift, sizeof(int), hipMemcpyDeviceToHost, st))) != TQ_OK) return r;
+    if ((r = hip_ok(hipMemcpyAsync(&shift, &h->shift, sizeof(int), hipMemcpyDeviceToHost, st))) != TQ_OK) return r;
     if ((r = hip_ok(hipStreamSynchronize(st))) != TQ_OK) return r;
     if (boundaries != nullptr)
         for (int j = 0; j < levels - 1; ++j) boundaries[j] = (centroids[j] + centroids[j + 1]) * 0.5;

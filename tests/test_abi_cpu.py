@@ -206,7 +206,12 @@ def test_batching_argument_validation():
 def test_lloyd_fit_argument_validation():
     import numpy as np
     L = tq.lib()
-    ws = int(L.tq_lloyd_max_workspace_bytes())
+    ws = int(L.tq_lloyd_max_workspace_bytes(10))
+    assert L.tq_lloyd_max_workspace_bytes(0) == -tq.TQ_E_SHAPE
+    assert L.tq_lloyd_max_workspace_bytes(1 << 31) == -tq.TQ_E_SHAPE
+    # the sorted keys (two buffers) and the prefix sums: at least 16 bytes a sample
+    assert L.tq_lloyd_max_workspace_bytes(1 << 20) >= 16 << 20
+    assert L.tq_lloyd_max_workspace_bytes(1 << 24) > L.tq_lloyd_max_workspace_bytes(1 << 20)
     assert ws > 256 * 8 * 4
     init = np.linspace(-1, 1, 4)
     c = np.zeros(4)

@@ -38,6 +38,9 @@ CASES = [
     ("one_sample", lambda r: np.array([0.3]), 2, (-1.0, 1.0), 5),
     ("no_iteration", lambda r: r.standard_normal(1000), 4, (-1.0, 1.0), 0),
     ("large_magnitude", lambda r: r.standard_normal(40000) * 1e6, 4, (-2e6, 2e6), 25),
+    ("signed_zeros", lambda r: np.concatenate([np.zeros(700), -np.zeros(900), r.standard_normal(5000)]), 4,
+     (-1.0, 1.0), 12),
+    ("few_distinct", lambda r: r.integers(-3, 4, 20000) * 0.5, 16, (-2.0, 2.0), 15),
 ]
 
 
@@ -61,7 +64,7 @@ def test_refit_printed_table_on_normal_samples(dev):
 
 
 def test_shared_workspace_and_non_finite_input(dev):
-    ws = torch.empty(int(tq.lib().tq_lloyd_max_workspace_bytes()), dtype=torch.uint8, device=dev)
+    ws = torch.empty(int(tq.lib().tq_lloyd_max_workspace_bytes(7000)), dtype=torch.uint8, device=dev)
     r = np.random.default_rng(9)
     run(dev, r.standard_normal(5000).astype(np.float32), 8, np.linspace(-2, 2, 8), 10, ws)
     run(dev, r.standard_normal(7000).astype(np.float32), 4, np.linspace(-1, 1, 4), 10, ws)
@@ -97,3 +100,12 @@ def test_full_size_bench_configuration(dev):
     dev_max = float(np.abs(c500 - gc).max())
     print(f"    500 iterations: max |c - density fit| = {dev_max:.2e}", flush=True)
     assert dev_max <= 5e-3, dev_max
+
+
+def test_samples_beyond_one_counting_round_per_segment(dev):
+    """More than 2^24 samples: each of the 32768 splitter segments then
+    holds more than 512 keys, and a boundary is narrowed down inside its
+    segment in device memory before the final count."""
+    n = (1 << 24) + 40961
+    x = np.random.default_rng(17).standard_normal(n).astype(np.float32)
+    run(dev, x, 16, tq.lloyd_max_table(4)[0].astype(np.float64), 3)

@@ -430,31 +430,42 @@ fit_prefix_kernel(const unsigned int *keys, int64_t n, const FitHead *h, const l
 // The iterations
 // ---------------------------------------------------------------------------
 
+// the value of v in lane `src` (uniform), through the scalar unit
+__device__ __forceinline__ long long lane_value(long long v, int src)
+{
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned int lo = (unsigned int)__builtin_amdgcn_readlane((int)(unsigned int)u, src);
+    const unsigned int hi = (unsigned int)__builtin_amdgcn_readlane((int)(unsigned int)(u >> 32), src);
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // The last window of sorted keys a wavefront counted for one boundary:
-// keys[glo .. glo + glen) (glen <= kSegMax) with keys[glo] <= K and the
-// first key above K in (glo, glo + glen]. Lane l holds keys glo + 64 e + l
-// and the prefix sums at those positions; the window is reused while it
-// still brackets the boundary (boundaries move little between late
-// iterations), which costs no memory access at all.
+// keys[glo .. glo + glen) (glen <= kSegMax) with keys[glo] <= K and the first
+// key above K in (glo, glo + glen]. Lane l holds keys glo + 64 e + l and
+// the prefix sums at those positions; the window is reused while it still
+// brackets the boundary (boundaries move little between late iterations),
+// which costs no memory access at all.
+constexpr int kWinR = kSegMax / 64; // keys (and prefix sums) per lane in a window
+
 struct Window {
     int64_t glo;
     int glen;
     unsigned int first;  // keys[glo]
     unsigned int next;   // keys[glo + glen], or 0xffffffff (above every key) at the end
     bool ok;
-    unsigned int kv[kSegMax / 64];   // 0xffffffff past the window
-    long long pv[kSegMax / 64 + 1];  // prefix[glo + 64 e + l] for 64 e + l <= glen
+    unsigned int kv[kWinR];  // 0xffffffff past the window
+    long long pv[kWinR + 1]; // prefix[glo + 64 e + l] for 64 e + l <= glen
 };
 
 // Position of boundary key K in the sorted keys (the number of keys <= K)
 // and the prefix sum there, computed by one wavefront (K is uniform).
 // spl[i] = keys[i * seg] for i < nsp. Each narrowing round probes 64
 // evenly spaced candidates and keeps the interval after the last one <= K.
-__device__ __forceinline__ void locate(const unsigned int *__restrict__ keys, const long long *__restrict__ prefix, int64_t n,
-                       int64_t seg, int nsp, const unsigned int *spl, unsigned int K, Window &w, int64_t &pos,
-                       long long &psum)
+__device__ __forceinline__ void locate(const unsigned int *__restrict__ keys, const long long *__restrict__ prefix,
+                                       int64_t n, int64_t seg, int nsp, const unsigned int *spl, unsigned int K,
+                                       Window &w, int64_t &pos, long long &psum)
 {
-    constexpr int R = kSegMax / 64;
+    constexpr int R = kWinR;
     const int lane = threadIdx.x & 63;
     if (!(w.ok && w.first <= K && K < w.next)) {
         // last splitter <= K, in LDS
@@ -491,30 +502,37 @@ __device__ __forceinline__ void locate(const unsigned int *__restrict__ keys, co
             glo += (c - 1) * stride;
             glen = min(stride, glen - (c - 1) * stride);
         }
+        const int64_t wlo = glo, wlen = glen;
         // the window's keys and the prefix sums at every candidate position,
         // in one round of loads
 #pragma unroll
         for (int e = 0; e < R; ++e) {
-            const int j = e * 64 + lane;
-            w.kv[e] = j < glen ? keys[glo + j] : 0xffffffffu;
-            w.pv[e] = j <= glen ? prefix[glo + j] : 0;
+            const int64_t j = e * 64 + lane;
+            w.kv[e] = j < wlen ? keys[wlo + j] : 0xffffffffu;
+            w.pv[e] = j <= wlen ? prefix[wlo + j] : 0;
         }
-        w.pv[R] = lane == 0 && R * 64 <= glen ? prefix[glo + R * 64] : 0;
-        w.next = glo + glen < n ? keys[glo + glen] : 0xffffffffu;
-        w.first = (unsigned int)__shfl((int)w.kv[0], 0);
-        w.glo = glo;
-        w.glen = (int)glen;
+        w.pv[R] = lane == 0 && R * 64 <= wlen ? prefix[wlo + R * 64] : 0;
+        w.next = wlo + wlen < n ? keys[wlo + wlen] : 0xffffffffu;
+        w.first = (unsigned int)__builtin_amdgcn_readfirstlane((int)w.kv[0]);
+        w.glo = wlo;
+        w.glen = (int)wlen;
         w.ok = true;
     }
     // the keys <= K are a prefix of the window
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < R; ++e) cnt += __popcll(__ballot(w.kv[e] <= K));
-    long long v = w.pv[0];
+    // the prefix sum at the position: entry cnt >> 6 of lane cnt & 63,
+    // broadcast entry by entry (a select over the entries with the uniform
+    // index would be compiled to an indexed copy in scratch memory)
+    long long v = 0;
 #pragma unroll
-    for (int e = 1; e <= R; ++e) v = (cnt >> 6) == e ? w.pv[e] : v;
+    for (int e = 0; e <= R; ++e) {
+        const long long x = lane_value(w.pv[e], cnt & 63);
+        v = (cnt >> 6) == e ? x : v;
+    }
     pos = w.glo + cnt;
-    psum = __shfl(v, cnt & 63);
+    psum = v;
 }
 
 // All iterations in one block. An iteration: one wavefront per boundary
@@ -630,6 +648,88 @@ fit_iterate_kernel(const unsigned int *__restrict__ keys, const long long *__res
     for (int k = t; k < levels; k += kIterThreads) h->cent[k] = cent[cur][k];
 }
 
+// Tables of up to 17 levels (one boundary per wavefront): every wavefront
+// holds all centroids (level k in lane k) and recomputes the new centroids
+// and boundary keys itself from the positions and sums the wavefronts
+// published, so an iteration needs one barrier. Positions and sums are
+// double-buffered by iteration parity: a wavefront can only start writing
+// a buffer again after every wavefront has passed the barrier of the
+// iteration in between.
+constexpr int kSmallLevels = kIterThreads / 64 + 1;
+
+// lane j: the key of boundary j (ascending), from the centroids in lanes
+// 0 .. levels - 1; lanes from levels - 1 on get 0xffffffff
+__device__ __forceinline__ unsigned int wave_boundary_keys(double c, int levels, unsigned int *sortbuf)
+{
+    const int lane = threadIdx.x & 63, nb = levels - 1;
+    const double cn = __shfl_down(c, 1);
+    unsigned int k = lane < nb ? boundary_key(c, cn) : 0xffffffffu;
+    const unsigned int kn = __shfl_down(k, 1);
+    if (__ballot(lane + 1 < nb && k > kn) != 0) {
+        // out of order (possible only through rounding): rank sort, equal
+        // keys by lane
+        int r = 0;
+        for (int i = 0; i < nb; ++i) {
+            const unsigned int o = (unsigned int)__builtin_amdgcn_readlane((int)k, i);
+            r += (o < k || (o == k && i < lane)) ? 1 : 0;
+        }
+        if (lane < nb) sortbuf[r] = k;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        k = lane < nb ? sortbuf[lane] : 0xffffffffu;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    return k;
+}
+
+__global__ void __launch_bounds__(kIterThreads)
+fit_iterate_small_kernel(const unsigned int *__restrict__ keys, const long long *__restrict__ prefix, int64_t n,
+                         int levels, int iterations, FitHead *h)
+{
+    const int s = h->shift;
+    if (s < 0) return;
+    constexpr int kWaves = kIterThreads / 64;
+    __shared__ unsigned int spl[kSplit];
+    __shared__ int64_t pos[2][kSmallLevels];
+    __shared__ long long psum[2][kSmallLevels];
+    __shared__ unsigned int sortbuf[kWaves][kSmallLevels];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t seg = (n + kSplit - 1) / kSplit;
+    const int nsp = (int)((n + seg - 1) / seg);
+    for (int i = t; i < nsp; i += kIterThreads) spl[i] = keys[(int64_t)i * seg];
+    const long long total = prefix[n];
+    const int nb = levels - 1;
+    double c = lane < levels ? h->cent[lane] : 0.0;
+    __syncthreads();
+    unsigned int K = wave_boundary_keys(c, levels, sortbuf[wave]);
+    Window win; // wavefront w's window for boundary w
+    win.ok = false;
+    for (int it = 0; it < iterations; ++it) {
+        const int b = it & 1;
+        if (wave < nb) {
+            const unsigned int Kw = (unsigned int)__builtin_amdgcn_readlane((int)K, wave);
+            int64_t p;
+            long long ps;
+            locate(keys, prefix, n, seg, nsp, spl, Kw, win, p, ps);
+            if (lane == 0) {
+                pos[b][wave] = p;
+                psum[b][wave] = ps;
+            }
+        }
+        __syncthreads();
+        if (lane < levels) {
+            const int64_t hi = lane < nb ? pos[b][lane] : n, lo = lane > 0 ? pos[b][lane - 1] : 0;
+            const long long shi = lane < nb ? psum[b][lane] : total, slo = lane > 0 ? psum[b][lane - 1] : 0;
+            if (hi > lo) c = ldexp((double)(shi - slo), -s) / (double)(hi - lo);
+        }
+        K = wave_boundary_keys(c, levels, sortbuf[wave]);
+    }
+    if (wave == 0 && lane < levels) h->cent[lane] = c;
+}
+
 int32_t hip_ok(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_HIP; }
 
 } // namespace
@@ -711,8 +811,13 @@ int32_t tq_lloyd_max_fit(const float *samples, int64_t n, int32_t levels, const 
             hipLaunchKernelGGL(fit_prefix_kernel<false>, dim3(tiles), dim3(kThreads), 0, st, keys_a, n, h, tile_sum,
                                prefix);
         }
-        hipLaunchKernelGGL(fit_iterate_kernel, dim3(1), dim3(kIterThreads), 0, st, keys_a, prefix, n, levels,
-                           iterations, h);
+        if (levels <= kSmallLevels) {
+            hipLaunchKernelGGL(fit_iterate_small_kernel, dim3(1), dim3(kIterThreads), 0, st, keys_a, prefix, n, levels,
+                               iterations, h);
+        } else {
+            hipLaunchKernelGGL(fit_iterate_kernel, dim3(1), dim3(kIterThreads), 0, st, keys_a, prefix, n, levels,
+                               iterations, h);
+        }
     }
     if ((r = hip_ok(hipGetLastError())) != TQ_OK) return r;
     int shift = 0;

@@ -239,6 +239,20 @@ __global__ void __launch_bounds__(kThreads) fit_init_kernel(FitHead *h, int bloc
 // ... of its tile, so step i of a tile covers kThreads consecutive keys in
 // thread order. The first pass reads the samples and forms their keys.
 
+// The tile a block processes. Blocks are dispatched to the XCDs in turn
+// (block b to XCD b % 8), so tiles are dealt out in contiguous runs, one
+// run per XCD: neighbouring tiles then write neighbouring bytes (histogram
+// entries, runs of one digit, prefix sums) through the same L2, where
+// partly written lines merge instead of being written back from several.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t block_tile(int64_t tiles)
+{
+    const int64_t b = blockIdx.x, x = b % kXcds, k = b / kXcds;
+    const int64_t q = tiles / kXcds, r = tiles % kXcds;
+    return x * q + (x < r ? x : r) + k;
+}
+
 template <bool FROM_SAMPLES> __device__ __forceinline__ unsigned int load_key(const void *src, int64_t i)
 {
     if constexpr (FROM_SAMPLES) return float_key(static_cast<const float *>(src)[i]);
@@ -246,9 +260,9 @@ template <bool FROM_SAMPLES> __device__ __forceinline__ unsigned int load_key(co
 }
 
 template <bool FROM_SAMPLES>
-__device__ __forceinline__ void load_tile(const void *src, int64_t n, unsigned int (&key)[kItems])
+__device__ __forceinline__ void load_tile(const void *src, int64_t n, int64_t tile, unsigned int (&key)[kItems])
 {
-    const int64_t t0 = (int64_t)blockIdx.x * kTile + threadIdx.x;
+    const int64_t t0 = tile * kTile + threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const int64_t idx = t0 + (int64_t)i * kThreads;
@@ -264,10 +278,11 @@ fit_digit_count_kernel(const void *src, int64_t n, int sh, unsigned int *hist, i
     if (h->shift < 0) return;
     __shared__ unsigned int cnt[kDigits];
     cnt[threadIdx.x] = 0;
+    const int64_t tile = block_tile(tiles);
     unsigned int key[kItems];
-    load_tile<FROM_SAMPLES>(src, n, key);
+    load_tile<FROM_SAMPLES>(src, n, tile, key);
     __syncthreads();
-    const int64_t t0 = (int64_t)blockIdx.x * kTile + threadIdx.x;
+    const int64_t t0 = tile * kTile + threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const bool valid = t0 + (int64_t)i * kThreads < n;
@@ -277,7 +292,7 @@ fit_digit_count_kernel(const void *src, int64_t n, int sh, unsigned int *hist, i
         if (valid && (peers & lanes_below()) == 0) atomicAdd(&cnt[d], (unsigned int)__popcll(peers));
     }
     __syncthreads();
-    hist[(int64_t)threadIdx.x * tiles + blockIdx.x] = cnt[threadIdx.x];
+    hist[(int64_t)threadIdx.x * tiles + tile] = cnt[threadIdx.x];
 }
 
 // one block per digit: the digit's per-tile counts become exclusive
@@ -315,13 +330,14 @@ fit_digit_scatter_kernel(const void *src, int64_t n, int sh, const unsigned int 
     const int t = threadIdx.x, wave = t >> 6;
     unsigned int total;
     const unsigned int base = block_exclusive_scan<unsigned int>(h->digit_total[t], total);
-    start[t] = base + hist[(int64_t)t * tiles + blockIdx.x];
+    const int64_t tile = block_tile(tiles);
+    start[t] = base + hist[(int64_t)t * tiles + tile];
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) wcnt[w][t] = 0;
     unsigned int key[kItems];
-    load_tile<FROM_SAMPLES>(src, n, key);
+    load_tile<FROM_SAMPLES>(src, n, tile, key);
     __syncthreads();
-    const int64_t t0 = (int64_t)blockIdx.x * kTile + t;
+    const int64_t t0 = tile * kTile + t;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const bool valid = t0 + (int64_t)i * kThreads < n;
@@ -358,7 +374,8 @@ fit_tile_sum_kernel(const unsigned int *keys, int64_t n, const FitHead *h, long 
 {
     const int s = h->shift;
     if (s < 0) return;
-    const int64_t t0 = (int64_t)blockIdx.x * kTile + threadIdx.x;
+    const int64_t tile = block_tile((n + kTile - 1) / kTile);
+    const int64_t t0 = tile * kTile + threadIdx.x;
     long long acc = 0;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
@@ -367,7 +384,7 @@ fit_tile_sum_kernel(const unsigned int *keys, int64_t n, const FitHead *h, long 
     }
     long long total;
     block_exclusive_scan<long long>(acc, total);
-    if (threadIdx.x == 0) tile_sum[blockIdx.x] = total;
+    if (threadIdx.x == 0) tile_sum[tile] = total;
 }
 
 // one block: the tile sums become exclusive prefixes
@@ -400,7 +417,8 @@ fit_prefix_kernel(const unsigned int *keys, int64_t n, const FitHead *h, const l
     __shared__ long long q[kTile + kTile / kItems];
     auto slot = [](int j) { return j + (j >> 4); };
     const int t = threadIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.x * kTile;
+    const int64_t tile = block_tile((n + kTile - 1) / kTile);
+    const int64_t t0 = tile * kTile;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const int j = i * kThreads + t;
@@ -411,7 +429,7 @@ fit_prefix_kernel(const unsigned int *keys, int64_t n, const FitHead *h, const l
 #pragma unroll
     for (int k = 0; k < kItems; ++k) run += q[slot(t * kItems + k)];
     long long total;
-    long long acc = block_exclusive_scan<long long>(run, total) + tile_sum[blockIdx.x];
+    long long acc = block_exclusive_scan<long long>(run, total) + tile_sum[tile];
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         acc += q[slot(t * kItems + k)];
@@ -423,7 +441,7 @@ fit_prefix_kernel(const unsigned int *keys, int64_t n, const FitHead *h, const l
         const int j = i * kThreads + t;
         if (t0 + j < n) prefix[t0 + j + 1] = q[slot(j)];
     }
-    if (blockIdx.x == 0 && t == 0) prefix[0] = 0;
+    if (tile == 0 && t == 0) prefix[0] = 0;
 }
 
 // ---------------------------------------------------------------------------

@@ -41,6 +41,11 @@ CASES = [
     ("signed_zeros", lambda r: np.concatenate([np.zeros(700), -np.zeros(900), r.standard_normal(5000)]), 4,
      (-1.0, 1.0), 12),
     ("few_distinct", lambda r: r.integers(-3, 4, 20000) * 0.5, 16, (-2.0, 2.0), 15),
+    # the largest table of the one-boundary-per-wavefront kernel, and the
+    # smallest and a 5-bit one of the kernel whose wavefronts take several
+    ("levels_17", lambda r: r.standard_normal(70000), 17, (-2.6, 2.6), 30),
+    ("levels_18", lambda r: r.standard_normal(70000), 18, (-2.6, 2.6), 30),
+    ("levels_32", lambda r: r.standard_normal(200000), 32, (-3.0, 3.0), 40),
 ]
 
 

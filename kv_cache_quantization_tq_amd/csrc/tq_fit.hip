@@ -157,17 +157,21 @@ template <typename T> __device__ T block_exclusive_scan(T v, T &total)
 }
 
 // Lanes of the wavefront, among those with `valid`, whose digit equals this
-// lane's (eight votes, one per digit bit).
+// lane's (eight votes, one per digit bit). Per bit and 32-bit half of the
+// mask: m &= ~(vote ^ x) with x = all ones where this lane's bit is set,
+// one three-input bitwise instruction.
 __device__ __forceinline__ unsigned long long match_digit(unsigned int d, bool valid)
 {
-    unsigned long long m = __ballot(valid);
+    const unsigned long long v0 = __ballot(valid);
+    unsigned int lo = (unsigned int)v0, hi = (unsigned int)(v0 >> 32);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const unsigned long long v = __ballot(bit);
-        m &= bit ? v : ~v;
+        const unsigned int x = 0u - ((d >> b) & 1u);
+        const unsigned long long v = __ballot(x != 0u);
+        lo &= ~((unsigned int)v ^ x);
+        hi &= ~((unsigned int)(v >> 32) ^ x);
     }
-    return m;
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 // ---------------------------------------------------------------------------
@@ -283,14 +287,12 @@ fit_digit_count_kernel(const void *src, int64_t n, int sh, unsigned int *hist, i
     load_tile<FROM_SAMPLES>(src, n, tile, key);
     __syncthreads();
     const int64_t t0 = tile * kTile + threadIdx.x;
+    // counting needs no order: one LDS add per key (lanes adding to the
+    // same digit are serialised by the LDS, which costs less than matching
+    // the lanes' digits first)
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const bool valid = t0 + (int64_t)i * kThreads < n;
-        const unsigned int d = (key[i] >> sh) & 255u;
-        const unsigned long long peers = match_digit(d, valid);
-        // one LDS add per distinct digit of the wavefront
-        if (valid && (peers & lanes_below()) == 0) atomicAdd(&cnt[d], (unsigned int)__popcll(peers));
-    }
+    for (int i = 0; i < kItems; ++i)
+        if (t0 + (int64_t)i * kThreads < n) atomicAdd(&cnt[(key[i] >> sh) & 255u], 1u);
     __syncthreads();
     hist[(int64_t)threadIdx.x * tiles + tile] = cnt[threadIdx.x];
 }
@@ -318,26 +320,43 @@ __global__ void __launch_bounds__(kThreads) fit_digit_scan_kernel(unsigned int *
 // Stable scatter of a tile: a key goes to (keys of smaller digits) + (keys
 // of its digit in earlier tiles) + (keys of its digit earlier in this
 // tile). Within a step the earlier keys of the same digit are those of
-// lower lanes of the same wavefront and of lower wavefronts.
+// lower lanes of the same wavefront and of lower wavefronts. The tile is
+// first arranged in LDS in that order (digit by digit), then written out
+// with consecutive threads writing consecutive positions of each digit's
+// run, rather than each key on its own.
 template <bool FROM_SAMPLES>
 __global__ void __launch_bounds__(kThreads)
 fit_digit_scatter_kernel(const void *src, int64_t n, int sh, const unsigned int *hist, int64_t tiles,
                          const FitHead *h, unsigned int *dst)
 {
     if (h->shift < 0) return;
-    __shared__ unsigned int start[kDigits];
+    __shared__ unsigned int start[kDigits];  // destination of the tile's first key of each digit
+    __shared__ unsigned int lbase[kDigits];  // place of that key in the arranged tile
+    __shared__ unsigned int run[kDigits];    // keys of each digit arranged so far
     __shared__ unsigned int wcnt[kThreads / 64][kDigits];
+    __shared__ unsigned int arranged[kTile];
     const int t = threadIdx.x, wave = t >> 6;
-    unsigned int total;
-    const unsigned int base = block_exclusive_scan<unsigned int>(h->digit_total[t], total);
     const int64_t tile = block_tile(tiles);
-    start[t] = base + hist[(int64_t)t * tiles + tile];
+    const int64_t t0 = tile * kTile + t;
+    const int nvalid = (int)min((int64_t)kTile, n - tile * kTile);
+    run[t] = 0;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) wcnt[w][t] = 0;
     unsigned int key[kItems];
     load_tile<FROM_SAMPLES>(src, n, tile, key);
     __syncthreads();
-    const int64_t t0 = tile * kTile + t;
+    // the tile's keys per digit, then where each digit's keys begin in the
+    // arranged tile and in the destination
+#pragma unroll
+    for (int i = 0; i < kItems; ++i)
+        if (t0 + (int64_t)i * kThreads < n) atomicAdd(&run[(key[i] >> sh) & 255u], 1u);
+    __syncthreads();
+    unsigned int total;
+    lbase[t] = block_exclusive_scan<unsigned int>(run[t], total);
+    const unsigned int base = block_exclusive_scan<unsigned int>(h->digit_total[t], total);
+    start[t] = base + hist[(int64_t)t * tiles + tile];
+    run[t] = 0;
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         const bool valid = t0 + (int64_t)i * kThreads < n;
@@ -347,9 +366,9 @@ fit_digit_scatter_kernel(const void *src, int64_t n, int sh, const unsigned int 
         if (valid && rank == 0) wcnt[wave][d] = (unsigned int)__popcll(peers);
         __syncthreads();
         if (valid) {
-            unsigned int p = start[d] + rank;
+            unsigned int p = lbase[d] + run[d] + rank;
             for (int w = 0; w < wave; ++w) p += wcnt[w][d];
-            dst[p] = key[i];
+            arranged[p] = key[i];
         }
         __syncthreads();
         unsigned int step = 0;
@@ -358,8 +377,18 @@ fit_digit_scatter_kernel(const void *src, int64_t n, int sh, const unsigned int 
             step += wcnt[w][t];
             wcnt[w][t] = 0;
         }
-        start[t] += step;
+        run[t] += step;
         __syncthreads();
+    }
+    // key j of the arranged tile goes to start[d] + (j - lbase[d])
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int jj = i * kThreads + t;
+        if (jj < nvalid) {
+            const unsigned int k = arranged[jj];
+            const unsigned int d = (k >> sh) & 255u;
+            dst[start[d] + (unsigned int)jj - lbase[d]] = k;
+        }
     }
 }
 

@@ -250,7 +250,7 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
  * --------------------------------------------------------------------- */
 
 /* Bytes of device workspace tq_lloyd_max_fit needs for n samples (host
- * only; 16 * n plus about 1.3 KB per 4096 samples). Returns -TQ_E_SHAPE
+ * only; 16 * n plus about 1 KB per 4096 samples). Returns -TQ_E_SHAPE
  * when n is outside 1 .. 2^31 - 1. */
 int64_t tq_lloyd_max_workspace_bytes(int64_t n);
 

@@ -4,8 +4,8 @@
     python -m kv_cache_quantization_tq_amd.profiling traffic <fetch.csv> <write.csv> \
         --copy-mib 512 [--json out.json] [--ops merge=N]
 
-``trace`` prints per-kernel dispatch counts and average / median / min
-durations from a ``--kernel-trace`` CSV, and with ``--stats`` the codec
+``trace`` prints per-kernel dispatch counts and average / median / 10th
+and 90th percentile / min durations from a ``--kernel-trace`` CSV, and with ``--stats`` the codec
 kernels' rows of rocprofv3's own ``--stats`` table. ``traffic`` turns the FETCH_SIZE and
 WRITE_SIZE counters (KiB per dispatch) of two ``--pmc`` runs of
 ``bench.py --copy-calibration-mib N`` into HBM bytes per launch: each
@@ -63,15 +63,24 @@ def read_trace(path: str):
     return out
 
 
+def percentile(d, q: float) -> float:
+    """Nearest-rank q-th percentile (0 < q <= 100) of a non-empty sample."""
+    s = sorted(d)
+    k = -(-q * len(s) // 100)  # ceil(q n / 100)
+    return s[min(len(s), max(1, int(k))) - 1]
+
+
 def trace_summary(path: str, ops: dict | None = None) -> str:
     rows = []
     tr = read_trace(path)
     for name, d in tr.items():
         if kernel_kind(name) in KINDS:
-            rows.append((name, len(d), sum(d) / len(d), statistics.median(d), min(d)))
-    lines = [f"{'kernel':70s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} {'min_us':>8s}"]
-    for name, n, avg, med, mn in sorted(rows):
-        lines.append(f"{name[:70]:70s} {n:5d} {avg:8.2f} {med:8.2f} {mn:8.2f}")
+            rows.append((name, len(d), sum(d) / len(d), statistics.median(d), percentile(d, 10), percentile(d, 90),
+                         min(d)))
+    lines = [f"{'kernel':70s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} {'p10_us':>8s} {'p90_us':>8s} "
+             f"{'min_us':>8s}"]
+    for name, n, avg, med, p10, p90, mn in sorted(rows):
+        lines.append(f"{name[:70]:70s} {n:5d} {avg:8.2f} {med:8.2f} {p10:8.2f} {p90:8.2f} {mn:8.2f}")
     for kind, n in (ops or {}).items():
         tot = sum(sum(d) for name, d in tr.items() if kernel_kind(name) == kind)
         lines.append(f"{kind}: {n} operations, {tot / n:.2f} us of kernel time per operation")

@@ -19,8 +19,10 @@
 // that order; every iteration then locates each boundary in the sorted keys
 // (a splitter table in LDS, then one segment of keys) and reads counts and
 // sums as differences of positions and prefix sums. All iterations run in
-// one launch of a single block; the samples are read five times in all,
-// not once per iteration.
+// one launch of a single block. The set-up reads the samples three times
+// and the keys eight times, whatever the number of iterations; an
+// iteration reads a few windows of keys and sums, none when the boundaries
+// stay inside the windows already held.
 //
 // Determinism: each sample enters the sums as the exact integer
 // rint(x * 2^s), with s chosen from the sample count and the largest

@@ -12,7 +12,6 @@ import pytest
 import oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-PAGE = "/root/reference/PAPER.md"
 
 
 def read_signs():
@@ -108,14 +107,66 @@ def test_three_bit_table_is_the_textbook_gaussian_quantiser():
     assert bd[3] == 0.0
 
 
-@pytest.mark.skipif(not os.path.exists(PAGE), reason="page text not mounted")
-def test_golden_tables_are_the_page_text():
-    page = open(PAGE).read()
-    for b, t in read_lloyd_max().items():
+def page_tables(text):
+    """The printed SIGN_VECTORS and LLOYD_MAX tables of the page "mlx-bun
+    0.0.9 -> 0.0.11" (turboquant-tables.ts) as decimal strings, parsed from
+    the page's text (diff lines carry a leading '+')."""
+    import re
+    lines = [ln[1:] if ln.startswith("+") else ln for ln in text.splitlines()]
+    body = "\n".join(lines)
+    sv = body[body.index("export const SIGN_VECTORS"):]
+    sv = sv[:sv.index("\n};")]
+    signs = {}
+    for m in re.finditer(r"^\s*(\d+): \[(.*?)\]", sv, re.S | re.M):
+        signs[int(m.group(1))] = re.findall(r"-?\d+", m.group(2))
+    lm = body[body.index("export const LLOYD_MAX"):]
+    lm = lm[:lm.index("\n};")]
+    tables = {}
+    for m in re.finditer(r"^\s*(\d+): \{(.*?)^\s*\},", lm, re.S | re.M):
+        t = {}
         for kind in ("centroids", "boundaries"):
-            assert ", ".join(t[kind][:3]) in page
-    for d, txt in read_signs().items():
-        assert f"{d}: [" in page
+            k = re.search(kind + r": \[(.*?)\]", m.group(2), re.S)
+            t[kind] = re.findall(r"-?[0-9][0-9.e+-]*", k.group(1))
+        tables[int(m.group(1))] = t
+    return signs, tables
+
+
+PAGE_TEXT = os.environ.get("TQ_PAGE_TEXT", "")
+
+
+@pytest.mark.skipif(not os.path.isfile(PAGE_TEXT),
+                    reason="set TQ_PAGE_TEXT to the text of the tables page to compare the golden files with it")
+def test_golden_tables_are_the_page_text():
+    """Every printed value: each sign of every head_dim and each centroid and
+    boundary of every width, as decimal text, equals the golden files."""
+    signs, tables = page_tables(open(PAGE_TEXT).read())
+    golden_signs = read_signs()
+    assert sorted(signs) == sorted(golden_signs) == [64, 128, 256, 512]
+    for d in signs:
+        assert len(signs[d]) == d
+        assert signs[d] == golden_signs[d], d
+    golden = read_lloyd_max()
+    assert sorted(tables) == sorted(golden) == [2, 3, 4, 5, 8]
+    for b in tables:
+        for kind in ("centroids", "boundaries"):
+            assert tables[b][kind] == golden[b][kind], (b, kind)
+            assert len(tables[b][kind]) == 2 ** b - (kind == "boundaries")
+
+
+def test_page_table_parser_reads_a_printed_block():
+    """The parser above on a block laid out as the page prints it (values
+    here are placeholders, not the page's), so the page comparison cannot
+    pass vacuously."""
+    text = "\n".join([
+        "+export const SIGN_VECTORS: Record<TurboQuantHeadDim, number[]> = {",
+        "+  64: [", "+  1, -1,", "+  -1, 1,", "+  ],", "+};",
+        "+export const LLOYD_MAX: Record<TurboQuantValueBits, LloydMaxTable> = {",
+        "+  2: {", "+    centroids: [", "+  -1.5, -0.25, 0.25, 1.5,", "+    ],",
+        "+    boundaries: [", "+  -0.875, 0, 0.875,", "+    ],", "+  },", "+};",
+    ])
+    signs, tables = page_tables(text)
+    assert signs == {64: ["1", "-1", "-1", "1"]}
+    assert tables == {2: {"centroids": ["-1.5", "-0.25", "0.25", "1.5"], "boundaries": ["-0.875", "0", "0.875"]}}
 
 
 # ------------------------------------------------------------- conversions

@@ -69,6 +69,15 @@ DESCRIPTION = {
                    "cache to bf16",
     "joint_large": "joint_large: batch 4 x 65536 tokens, 8 KV heads, head_dim 512, bf16 N(0,1) with 1% of "
                    "rows zeroed; values 8-bit (unpacked bytes), keys 4-bit; one joint K/V decode to bf16",
+    "prefill_decode": "prefill_decode: the prefill cache (batch 1, 8 KV heads, head_dim 128, 32768 tokens, values "
+                      "4-bit, keys 4-bit) decoded to bf16 K and V alone, rotating over buffer sets so that the "
+                      "packed planes are read from HBM",
+    "long_k8v3": "long_k8v3: the ops page's specialised long-sequence decode configuration (tryDecodePackedKv: "
+                 "head_dim 256, 8-bit signed keys, 3-bit values, >= 8192 tokens): 32768 tokens x 8 KV heads from "
+                 "fp32 N(0,1), one joint K/V decode to bf16",
+    "deferred_v": "deferred_v: the long_decode cache (131072 tokens x 8 KV heads, head_dim 256, V5/K4) decoded "
+                  "with values left in the rotated domain (decodeValuesRotated), then one attention output of 32 "
+                  "query heads un-rotated (unrotateValues); the eager decode is timed alongside",
     "batch_merge": "batch_merge: 32 packed caches (8 KV heads, head_dim 128, V4/K4 planes of seeded random "
                    "bytes) of 4096..32768 tokens merged into one left-padded batch",
     "lloyd_fit": "lloyd_fit: 4-bit (16-level) Lloyd-Max table fitted to 2^24 N(0,1) float32 samples, 500 "
@@ -83,6 +92,10 @@ METRIC = {
     "long_decode": "KV tokens/sec decoded per step (append 1 token + full decode, d=256, V5/K4) and "
                    "achieved HBM GB/s vs peak",
     "joint_large": "KV tokens/sec joint K/V decode (d=512, V8/K4) and achieved HBM GB/s vs peak",
+    "prefill_decode": "KV tokens/sec decode alone (d=128, 4-bit, planes from HBM) and achieved HBM GB/s vs peak",
+    "long_k8v3": "KV tokens/sec joint K/V decode (d=256, K8 signed, V3, 32768 tokens) and achieved HBM GB/s vs peak",
+    "deferred_v": "KV tokens/sec decoded with deferred value un-rotation (d=256, V5/K4) and achieved HBM GB/s vs "
+                  "peak",
     "batch_merge": "KV tokens/sec merged into a left-padded batch (d=128, V4/K4 planes) and achieved HBM GB/s "
                    "vs peak",
     "lloyd_fit": "Lloyd-Max fit sample-iterations/sec (16 levels, 2^24 samples) and achieved HBM GB/s vs peak",
@@ -108,6 +121,11 @@ def traffic_file(workload):
     return os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
 
 
+def kernel_kind_of(name):
+    """The kind (profiling/build vocabulary) of a bench kernel name."""
+    return {"append": "encode", "merge": "merge", "fit": "fit", "attention": "attention"}.get(name, name)
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed counter runs, if they were
     taken on the current kernel source."""
@@ -121,6 +139,21 @@ def measured_traffic(workload, kernel):
     if not k or k.get("source_sha256") != source_digest(kernel):
         return None
     return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def committed_trace(workload, kernel):
+    """The kernel-trace figures of `kernel` in profiles/<workload>_kernel_trace.json,
+    if they were taken on the kernel's current sources."""
+    try:
+        with open(os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.json")) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    from kv_cache_quantization_tq_amd.build import source_digest
+    k = t.get(kernel)
+    if not k or k.get("source_sha256") != source_digest(kernel):
+        return None
+    return k
 
 
 def device_copy_gbps(torch, dev, mib=256, nbuf=6, reps=20):
@@ -148,8 +181,18 @@ def device_copy_gbps(torch, dev, mib=256, nbuf=6, reps=20):
 # ---------------------------------------------------------------------------
 
 def _oracle_threads():
-    n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    """Threads for the oracle: the host CPUs this process may run on, at most
+    16 (the host share of one GPU on the machines this runs on)."""
+    return max(1, min(16, host_cpus()["cpus_usable"]))
+
+
+def host_cpus():
+    """The host's CPU count and how many this process may run on."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"host_cpus": os.cpu_count() or 1, "cpus_usable": usable}
 
 
 def _par(fn, rows, threads):
@@ -197,7 +240,7 @@ def cpu_baseline(w, kn, vn, do_encode, do_decode, tokens_per_row):
     what = " + ".join(s for s, on in (("encode", do_encode), ("decode", do_decode)) if on)
     log(f"cpu oracle ({what}, {rows} rows): 1 thread {t1:.2f} s, {nt} threads {tn:.2f} s")
     return {"value": kv_tok / tn, "unit": "KV tokens/s", "cores": nt, "kind": "oracle",
-            "value_1_thread": kv_tok / t1,
+            "value_1_thread": kv_tok / t1, **host_cpus(),
             "sample": f"{what} of {rows} rows ({rows // w.heads} tokens x {w.heads} heads) of this workload, "
                       f"rows split over {nt} threads (single-thread figure alongside)"}
 
@@ -310,7 +353,7 @@ def setup_long_decode(torch, tq, W, w, dev, max_steps):
 
 def setup_joint(torch, tq, W, w, dev):
     k, v = W.make_kv(w, dev)
-    planes = tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits)
+    planes = tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed)
     torch.cuda.synchronize()
     ns = 16384 * w.heads  # rows of the oracle sample: the first 16384 tokens
     sample = (W.to_oracle(k.view(-1, w.head_dim)[:ns]), W.to_oracle(v.view(-1, w.head_dim)[:ns]))
@@ -323,7 +366,7 @@ def setup_joint(torch, tq, W, w, dev):
         if ev is not None:
             ev[0].record()
         tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
-                     k_bits=w.k_bits, k_out=ko, v_out=vo)
+                     k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
 
     _, dec_b = row_bytes(w)
     cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
@@ -333,6 +376,111 @@ def setup_joint(torch, tq, W, w, dev):
 def codec_config(w):
     return {"workload": DESCRIPTION[w.name], "tokens": w.kv_tokens, "heads": w.heads, "head_dim": w.head_dim,
             "v_bits": w.v_bits, "k_bits": w.k_bits, "k_signed": w.k_signed, "input_dtype": w.dtype}
+
+
+def setup_decode_only(torch, tq, W, w, dev, sets_hint):
+    """Decode alone, rotating over buffer sets of planes encoded beforehand
+    (untimed), so that each step reads its planes from HBM."""
+    k0, v0 = W.make_kv(w, dev)
+    _, dec_b = row_bytes(w)
+    per_set = w.rows * dec_b
+    nsets = sets_hint or max(2, math.ceil(1.5 * 2 ** 30 / per_set))
+    sets = []
+    for s in range(nsets):
+        planes = tq.encode_kv(k0, v0, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed)
+        sets.append((planes, torch.empty_like(k0, dtype=torch.bfloat16), torch.empty_like(v0, dtype=torch.bfloat16)))
+    torch.cuda.synchronize()
+    ns = min(w.rows, 65536)
+    sample = (W.to_oracle(k0.view(-1, w.head_dim)[:ns]), W.to_oracle(v0.view(-1, w.head_dim)[:ns]))
+    del k0, v0
+    log(f"workload {w.name}: {w.rows} rows, {nsets} plane sets of {per_set / 2**20:.0f} MiB (planes + outputs)")
+
+    def step(i, ev=None):
+        planes, ko, vo = sets[i % nsets]
+        if ev is not None:
+            ev[0].record()
+        tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
+                     k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
+
+    cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
+    return step, 1, {"decode": (0, 1, w.rows * dec_b)}, (lambda i: w.kv_tokens), cpu, \
+        {**codec_config(w), "workload": DESCRIPTION[w.name], "buffer_sets": nsets}
+
+
+def setup_deferred_v(torch, tq, W, dev, steps_total):
+    """Rotated-domain value decode plus one un-rotation of an attention
+    output per step; the eager decode (inverse transform for every token) of
+    the same cache is timed after the timed region for comparison."""
+    w = W.WORKLOADS["long_decode"]
+    T, H, d, hq = w.tokens, w.heads, w.head_dim, 32
+    k, v = W.make_kv(w, dev)
+    planes = tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits)
+    torch.cuda.synchronize()
+    ns = 32768
+    sample = (W.to_oracle(k[:ns]), W.to_oracle(v[:ns]))
+    del k, v
+    ko = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    att = torch.randn((1, hq, d), generator=g, device=dev)  # stands for an attention output over rotated values
+    att_out = torch.empty_like(att)
+    log(f"workload deferred_v: {T} tokens x {H} heads, rotated decode + un-rotation of {hq} rows")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo,
+                     rotated_v=True)
+        if ev is not None:
+            ev[1].record()
+        tq.unrotate_values(att, out=att_out)
+
+    def eager_us(reps=20):
+        """Average event time of the eager decode (values fully decoded)."""
+        ev = [HipEvent(ctypes_stream(torch)) for _ in range(reps + 1)]
+        for _ in range(3):
+            tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(reps):
+            tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps * 1e3
+
+    def cpu():
+        import oracle as O
+        kn, vn = sample
+        rows = ns * H
+        planes_h = O.encode_kv(kn.reshape(rows, d), vn.reshape(rows, d), head_dim=d, k_bits=w.k_bits,
+                               v_bits=w.v_bits)
+        O.decode_kv({n: p[:64] for n, p in planes_h.items()}, rows=64, head_dim=d, k_bits=w.k_bits,
+                    v_bits=w.v_bits, rotated_v=True)
+        att_h = att.cpu().numpy().reshape(-1, d)
+
+        def run(threads):
+            def dec(r0, r1):
+                O.decode_kv({n: p[r0:r1] for n, p in planes_h.items()}, rows=r1 - r0, head_dim=d,
+                            k_bits=w.k_bits, v_bits=w.v_bits, rotated_v=True)
+            t0 = time.perf_counter()
+            _par(dec, rows, threads)
+            O.unrotate(att_h, d)
+            return time.perf_counter() - t0
+
+        t1 = run(1)
+        nt = _oracle_threads()
+        tn = run(nt) if nt > 1 else t1
+        log(f"cpu oracle (rotated decode of {rows} rows + un-rotation): 1 thread {t1:.2f} s, {nt} threads {tn:.2f} s")
+        return {"value": ns / tn, "unit": "KV tokens/s", "cores": nt, "kind": "oracle", "value_1_thread": ns / t1,
+                **host_cpus(),
+                "sample": f"rotated decode of the first {ns} tokens x {H} heads plus one un-rotation, rows split "
+                          f"over {nt} threads (single-thread figure alongside)"}
+
+    _, dec_b = row_bytes(w)
+    kernels = {"decode": (0, 1, T * H * dec_b), "unrotate": (1, 2, 2 * hq * d * 4)}
+    config = {**codec_config(w), "workload": DESCRIPTION["deferred_v"], "q_heads": hq, "rotated_v": True}
+    return step, 2, kernels, (lambda i: T), cpu, config, eager_us
 
 
 def setup_batch_merge(torch, tq, W, dev):
@@ -371,7 +519,7 @@ def setup_batch_merge(torch, tq, W, dev):
         t = time.perf_counter() - t0
         ntok = sum(lens)
         log(f"cpu oracle (merge of all {len(lens)} caches, {ntok} tokens): {t:.2f} s")
-        return {"value": ntok / t, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": ntok / t, "unit": "KV tokens/s", "cores": 1, "kind": "oracle", **host_cpus(),
                 "sample": f"the whole merge of the {len(lens)} caches ({ntok} tokens), one thread (numpy)"}
 
     config = {"workload": DESCRIPTION["batch_merge"], "sequences": len(lens), "tokens": sum(lens), "width": width,
@@ -404,7 +552,7 @@ def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
         OL.fit_samples(xs, init, it)
         t = time.perf_counter() - t0
         log(f"cpu oracle (fit of {ns} samples, {it} iterations): {t:.2f} s")
-        return {"value": ns * it / t, "unit": "sample-iterations/s", "cores": 1, "kind": "oracle",
+        return {"value": ns * it / t, "unit": "sample-iterations/s", "cores": 1, "kind": "oracle", **host_cpus(),
                 "sample": f"{it} iterations on the first {ns} samples, one thread (numpy)"}
 
     config = {"workload": DESCRIPTION["lloyd_fit"], "samples": n, "levels": levels, "iterations": iterations}
@@ -456,7 +604,7 @@ def setup_attn_decode(torch, tq, W, dev):
         OA.attention_decode(qh, kd, vr, 1, ns, None, H, 1.0 / np.sqrt(d))
         t = time.perf_counter() - t0
         log(f"cpu oracle (decode + attention over {ns} tokens): {t:.2f} s")
-        return {"value": ns / t, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": ns / t, "unit": "KV tokens/s", "cores": 1, "kind": "oracle", **host_cpus(),
                 "sample": f"decode + attention over the first {ns} tokens of the cache, one thread"}
 
     config = {"workload": DESCRIPTION["attn_decode"], "tokens": T, "kv_heads": H, "q_heads": hq, "head_dim": d,
@@ -495,10 +643,23 @@ def main():
     dev = torch.device("cuda:0")
     w = W.WORKLOADS.get(args.workload)
     steps = args.steps or {"long_decode": 20, "joint_large": 20, "batch_merge": 20, "lloyd_fit": 3,
-                           "attn_decode": 50}.get(args.workload, 50)
+                           "attn_decode": 50, "deferred_v": 20, "long_k8v3": 50,
+                           "prefill_decode": 50}.get(args.workload, 50)
 
+    extra = None
     if args.workload in ("prefill", "small_head"):
         step, marks, kernels, tokens, cpu_fn, config = setup_encode_decode(torch, tq, W, w, dev, args.sets)
+    elif args.workload == "prefill_decode":
+        w = W.WORKLOADS["prefill"]
+        w = W.Workload("prefill_decode", w.batch, w.tokens, w.heads, w.head_dim, w.dtype, w.v_bits, w.k_bits,
+                       w.k_signed, w.seed, w.kind)
+        step, marks, kernels, tokens, cpu_fn, config = setup_decode_only(torch, tq, W, w, dev, args.sets)
+    elif args.workload == "long_k8v3":
+        step, marks, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
+        config["workload"] = DESCRIPTION["long_k8v3"]
+    elif args.workload == "deferred_v":
+        step, marks, kernels, tokens, cpu_fn, config, extra = setup_deferred_v(torch, tq, W, dev,
+                                                                               args.warmup + steps)
     elif args.workload == "long_decode":
         step, marks, kernels, tokens, cpu_fn, config = setup_long_decode(torch, tq, W, w, dev,
                                                                          args.warmup + steps)
@@ -577,7 +738,22 @@ def main():
         f"device copy reference {copy_gbps:.0f} GB/s")
 
     dom = max(stats, key=lambda n: stats[n]["avg_us"])
+    extra_fields = {}
+    if extra is not None:
+        eager = extra()
+        extra_fields["eager_decode"] = {"avg_us": eager, "rotated_decode_plus_unrotate_us":
+                                        stats["decode"]["avg_us"] + stats["unrotate"]["avg_us"]}
+        log(f"eager decode (inverse transform of every token): {eager:.1f} us; rotated decode "
+            f"{stats['decode']['avg_us']:.1f} us + un-rotation {stats['unrotate']['avg_us']:.1f} us")
     cpu = None if args.no_cpu_baseline else cpu_fn()
+    # the committed kernel trace of this workload on the same sources, beside
+    # the live event figures (which include the dispatch gap before a kernel)
+    tr = committed_trace(args.workload, kernel_kind_of(dom))
+    trace_fields = None if tr is None else {
+        "source": f"profiles/{args.workload}_kernel_trace.json", "avg_us": tr["avg_us"],
+        "frac": stats[dom]["bytes"] / (tr["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+        "p10_frac": stats[dom]["bytes"] / (tr["p90_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+        "p90_frac": stats[dom]["bytes"] / (tr["p10_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}
 
     out = {
         "metric": METRIC[args.workload],
@@ -595,13 +771,15 @@ def main():
         "config": config,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": stats[dom]["GBps"], "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": stats[dom]["GBps"] / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic(args.workload, dom),
-                     "algorithmic_bytes": stats[dom]["bytes"], "avg_kernel_us": stats[dom]["avg_us"]},
+                     "traffic": measured_traffic(args.workload, kernel_kind_of(dom)),
+                     "algorithmic_bytes": stats[dom]["bytes"], "avg_kernel_us": stats[dom]["avg_us"],
+                     "committed_trace": trace_fields},
         "kernels": {**stats, "step": {"GBps": step_gbps, "frac": step_gbps / PEAK_HBM_GBPS},
                     "device_copy_reference_GBps": copy_gbps},
         "graph_replay": None if graph_ms_per_step is None else {
             "ms_per_step": graph_ms_per_step, "value": kv_tokens / (steps * graph_ms_per_step * 1e-3)},
         "cpu_baseline": cpu,
+        **extra_fields,
     }
     print(json.dumps(out), flush=True)
 

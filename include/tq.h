@@ -65,7 +65,9 @@ enum {
     TQ_E_ALIGN = 4,    /* misaligned pointer, or dim * bits not a whole byte  */
     TQ_E_DTYPE = 5,    /* dtype not TQ_F32 / TQ_BF16                          */
     TQ_E_SHAPE = 6,    /* negative tokens, heads < 1, or row count overflow   */
-    TQ_E_HIP = 7       /* the HIP runtime reported an error at launch         */
+    TQ_E_HIP = 7,      /* the HIP runtime reported an error at launch         */
+    TQ_E_CAPTURE = 8   /* a batching call needing more than one launch was    */
+                       /* made on a stream that is capturing a graph          */
 };
 
 /* Element types of K/V inputs and decoded outputs. */
@@ -138,6 +140,15 @@ int32_t tq_unrotate_values(const void *x, void *out, int32_t dtype, int64_t rows
 int32_t tq_lloyd_max_table(int32_t bits, float *centroids, float *boundaries);
 int32_t tq_sign_vector(int32_t head_dim, float *signs);
 
+/* Host evaluation of the quotient the kernels use for key scales, zero
+ * points and key codes, compiled from the same source: q[i] = a[i] / b[i]
+ * from r = RN(1/b[i]) by one refinement step (q0 = a r, e = fma(-q0, b, a),
+ * q = fma(e, r, q0)), the sign of a zero result taken from a[i]. For b[i] > 0
+ * it equals the IEEE quotient wherever the kernels take it (|a r| < 1e30,
+ * b < 1e30; outside that they divide). For checking the quotient on the
+ * CPU. Host only. */
+int32_t tq_quotient_host(const float *a, const float *b, int64_t n, float *q);
+
 /* Host evaluation of the value bin search exactly as the kernels run it
  * (same code, compiled for the host: the table-driven search of the fast
  * path for |z| <= 6, the clamped general search otherwise): idx[i] = number
@@ -171,10 +182,13 @@ int32_t tq_value_bin_host(int32_t bits, const float *z, int64_t n, uint8_t *idx)
  *
  * Each launch carries up to 120 plane segments (source, destination,
  * bytes) as a kernel argument; a call needs one segment per plane and
- * per contiguous run of tokens. Capturing a call in a HIP graph has been
- * checked only where the call makes one launch; the replay of a graph of
- * calls making three launches each (32 merged caches) faulted on MI355X,
- * cause not established, so launch such calls directly.
+ * per contiguous run of tokens. Graph capture: a call that fits in one
+ * launch may be captured (checked by replaying such graphs); a call that
+ * needs more than one launch returns TQ_E_CAPTURE, before launching
+ * anything, when `stream` is capturing, because the replay of a graph of
+ * such calls (32 merged caches, three launches per call) faulted on
+ * MI355X with no cause established in this library's code. Launch those
+ * calls directly.
  * --------------------------------------------------------------------- */
 
 /* mergeQuantRows: stack n caches (srcs[i] holds lens[i] tokens) into dst,

@@ -29,14 +29,14 @@ HEAD_DIMS = (64, 128, 256, 512)
 VALUE_BITS = (2, 3, 4, 5, 8)
 KEY_BITS = (2, 3, 4, 5, 8)
 
-TQ_OK, TQ_E_NULL, TQ_E_HEAD_DIM, TQ_E_BITS, TQ_E_ALIGN, TQ_E_DTYPE, TQ_E_SHAPE, TQ_E_HIP = range(8)
+TQ_OK, TQ_E_NULL, TQ_E_HEAD_DIM, TQ_E_BITS, TQ_E_ALIGN, TQ_E_DTYPE, TQ_E_SHAPE, TQ_E_HIP, TQ_E_CAPTURE = range(9)
 TQ_F32, TQ_BF16 = 0, 1
 TQ_DECODE_ROTATED_V = 1
 
 # every symbol include/tq.h declares
 EXPORTS = (
     "tq_packed_dim", "tq_status_string", "tq_encode_kv", "tq_decode_kv", "tq_unrotate_values",
-    "tq_lloyd_max_table", "tq_sign_vector", "tq_value_bin_host",
+    "tq_lloyd_max_table", "tq_sign_vector", "tq_value_bin_host", "tq_quotient_host",
     "tq_merge_rows", "tq_extend_rows", "tq_extract_row", "tq_filter_rows",
     "tq_lloyd_max_workspace_bytes", "tq_lloyd_max_fit",
     "tq_attention_workspace_bytes", "tq_attention_decode",
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
             "tq_lloyd_max_table": (i32, [i32, P, P]),
             "tq_sign_vector": (i32, [i32, P]),
             "tq_value_bin_host": (i32, [i32, P, i64, P]),
+            "tq_quotient_host": (i32, [P, P, i64, P]),
             "tq_merge_rows": (i32, [ctypes.POINTER(TQPackedKV), P, i32, i64, i32, ctypes.POINTER(TQConfig),
                                     ctypes.POINTER(TQPackedKV), P, P]),
             "tq_extend_rows": (i32, [ctypes.POINTER(TQPackedKV), i32, i64, P, ctypes.POINTER(TQPackedKV), i64,
@@ -140,6 +141,20 @@ def value_bin_host(bits: int, z):
     st = lib().tq_value_bin_host(bits, z.ctypes.data, z.size, out.ctypes.data)
     if st:
         raise TQError(st, f"value_bin_host(bits={bits})")
+    return out
+
+
+def quotient_host(a, b):
+    """The kernels' exact quotient a / b evaluated on the host (for CPU checks)."""
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    b = np.ascontiguousarray(b, dtype=np.float32).ravel()
+    if a.size != b.size:
+        raise ValueError("quotient_host: a and b differ in size")
+    out = np.zeros(a.size, np.float32)
+    st = lib().tq_quotient_host(a.ctypes.data, b.ctypes.data, a.size, out.ctypes.data)
+    if st:
+        raise TQError(st, "quotient_host")
     return out
 
 

@@ -134,6 +134,7 @@ const char *tq_status_string(int32_t status)
     case TQ_E_DTYPE: return "dtype must be TQ_F32 or TQ_BF16";
     case TQ_E_SHAPE: return "tokens must be >= 0 and heads >= 1 (row count within range)";
     case TQ_E_HIP: return "HIP runtime error at kernel launch";
+    case TQ_E_CAPTURE: return "batching call needs more than one launch and its stream is capturing a graph";
     default: return "unknown status";
     }
 }
@@ -247,6 +248,14 @@ int32_t tq_sign_vector(int32_t head_dim, float *signs)
     const uint32_t *m = head_dim == 64 ? kSignMask64 : head_dim == 128 ? kSignMask128
                       : head_dim == 256 ? kSignMask256 : kSignMask512;
     for (int i = 0; i < head_dim; ++i) signs[i] = ((m[i / 32] >> (i % 32)) & 1u) ? -1.0f : 1.0f;
+    return TQ_OK;
+}
+
+int32_t tq_quotient_host(const float *a, const float *b, int64_t n, float *q)
+{
+    if (n < 0) return TQ_E_SHAPE;
+    if (n > 0 && (a == nullptr || b == nullptr || q == nullptr)) return TQ_E_NULL;
+    for (int64_t i = 0; i < n; ++i) q[i] = quot_signed(a[i], b[i], 1.0f / b[i]);
     return TQ_OK;
 }
 

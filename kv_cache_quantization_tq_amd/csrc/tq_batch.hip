@@ -152,6 +152,14 @@ class Segments {
 
     int32_t launch(void *stream) const
     {
+        // A graph replay of calls making several launches each faulted on
+        // MI355X (cause not established): such calls refuse capture before
+        // launching anything.
+        if (segs_.size() > (size_t)kMaxSegs) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess) return TQ_E_HIP;
+            if (cs != hipStreamCaptureStatusNone) return TQ_E_CAPTURE;
+        }
         for (size_t a = 0; a < segs_.size(); a += kMaxSegs) {
             SegList L{};
             L.count = (int32_t)std::min<size_t>(kMaxSegs, segs_.size() - a);

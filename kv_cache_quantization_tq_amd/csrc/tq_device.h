@@ -20,19 +20,24 @@
 // loads its group as 16-byte vectors and writes exactly 4*bits bytes of
 // packed codes plus one fp16 scale (and zero point).
 //
-// Exactness. Every arithmetic step rounds exactly as the plain binary32
-// definition does: butterflies in span order 1, 2, 4, ..., the single
-// multiply by binary32(1/sqrt(d)) at the end, sequential sums of squares,
-// no contraction (built with -ffp-contract=off), IEEE division and square
-// root per group, and per element a quotient a/b obtained as
+// Exactness. Every arithmetic step that feeds a stored plane rounds exactly
+// as the plain binary32 definition does: butterflies in span order 1, 2, 4,
+// ..., the single multiply by binary32(1/sqrt(d)) at the end, sequential
+// sums of squares, no contraction (built with -ffp-contract=off), IEEE
+// square root per group, and quotients a/b obtained as
 //   q0 = a*r, e = fma(-q0, b, a), q = fma(e, r, q0),  r = RN(1/b),
 // which equals the correctly rounded a/b whenever nothing overflows or
 // underflows (reciprocal refinement, Markstein 1990); groups outside that
-// range take the IEEE division instead. The value bin (number of boundaries
-// strictly below z) comes from a uniform-grid table built at compile time
-// whose cells are narrower than the closest pair of boundaries, so one
-// final comparison against the single boundary a cell may hold gives the
-// exact count.
+// range take the IEEE division instead. So key codes, key scales and zero
+// points and value scales are bit-exact. The one exception is the value
+// bin's argument z = y / (rms + 1e-8): it is taken as the single product
+// y * RN(1/(rms + 1e-8)), within 1.5 ulp of the quotient (|z| < 6, so
+// within 5e-7), which can move a code by one bin only for a z that close to
+// a boundary -- inside the codec's tolerance of an off-by-one bin within
+// 1e-5 of a boundary. The value bin (number of boundaries strictly below z)
+// comes from a uniform-grid table built at compile time whose cells are
+// narrower than the closest pair of boundaries, so one final comparison
+// against the single boundary a cell may hold gives the count for that z.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -195,6 +200,49 @@ template <> __device__ __forceinline__ uint32_t dev_sign<64>(int g) { return dSi
 template <> __device__ __forceinline__ uint32_t dev_sign<128>(int g) { return dSign128.m[g]; }
 template <> __device__ __forceinline__ uint32_t dev_sign<256>(int g) { return dSign256.m[g]; }
 template <> __device__ __forceinline__ uint32_t dev_sign<512>(int g) { return dSign512.m[g]; }
+
+// The sign vector as XOR masks in the layout of a loaded group: for bf16
+// data one dword per element pair (bit 15 flips the even element, bit 31
+// the odd one), for binary32 data one dword per element (bit 31). The
+// encoder copies its head_dim's table to LDS once per block and each lane
+// reads the masks of its group there, which costs no arithmetic per tile.
+template <int D, bool BF16> struct SignXor {
+    static constexpr int W = BF16 ? kGroup / 2 : kGroup; // dwords per group
+    uint32_t m[D / kGroup][W];
+    constexpr SignXor() : m{}
+    {
+        for (int g = 0; g < D / kGroup; ++g) {
+            const uint32_t s = SignTab<D>::m[g];
+            for (int k = 0; k < W; ++k)
+                m[g][k] = BF16 ? ((((s >> (2 * k)) & 1u) << 15) | (((s >> (2 * k + 1)) & 1u) << 31))
+                               : (((s >> k) & 1u) << 31);
+        }
+    }
+};
+
+__constant__ SignXor<64, true> dSx64b = SignXor<64, true>();
+__constant__ SignXor<128, true> dSx128b = SignXor<128, true>();
+__constant__ SignXor<256, true> dSx256b = SignXor<256, true>();
+__constant__ SignXor<512, true> dSx512b = SignXor<512, true>();
+__constant__ SignXor<64, false> dSx64f = SignXor<64, false>();
+__constant__ SignXor<128, false> dSx128f = SignXor<128, false>();
+__constant__ SignXor<256, false> dSx256f = SignXor<256, false>();
+__constant__ SignXor<512, false> dSx512f = SignXor<512, false>();
+
+template <int D, bool BF16> __device__ __forceinline__ const uint32_t *dev_sign_xor()
+{
+    if constexpr (BF16) {
+        if constexpr (D == 64) return &dSx64b.m[0][0];
+        else if constexpr (D == 128) return &dSx128b.m[0][0];
+        else if constexpr (D == 256) return &dSx256b.m[0][0];
+        else return &dSx512b.m[0][0];
+    } else {
+        if constexpr (D == 64) return &dSx64f.m[0][0];
+        else if constexpr (D == 128) return &dSx128f.m[0][0];
+        else if constexpr (D == 256) return &dSx256f.m[0][0];
+        else return &dSx512f.m[0][0];
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Scalar helpers
@@ -520,12 +568,22 @@ __device__ __forceinline__ void group_min_max(const float (&x)[kGroup], float &m
     mx = b;
 }
 
-// quotient a / b rounded to nearest, from r = RN(1/b) (see file header)
-__device__ __forceinline__ float quot(float a, float b, float r)
+// quotient a / b rounded to nearest, from r = RN(1/b) (see file header);
+// a zero quotient may come out as +0 for a = -0 (the last fma adds +0 and
+// -0), which does not matter where the result is rounded to an integer code
+__host__ __device__ __forceinline__ float quot(float a, float b, float r)
 {
     const float q0 = a * r;
     const float e = __builtin_fmaf(-q0, b, a);
     return __builtin_fmaf(e, r, q0);
+}
+
+// the same quotient with the sign of a zero result kept, for b > 0: equal
+// to the IEEE a / b whenever quot is exact (a stored zero point or scale of
+// -0 stays -0)
+__host__ __device__ __forceinline__ float quot_signed(float a, float b, float r)
+{
+    return __builtin_copysignf(quot(a, b, r), a);
 }
 
 // x / se - zp for element j (IEEE division on the slow path)
@@ -598,6 +656,54 @@ __device__ __forceinline__ void key_codes(const float (&x)[kGroup], float se, fl
     }
 }
 
+// Codes of one key group when every element's rounded value is known to be
+// in the code range: the same arithmetic as key_codes without the clamp
+// (the unsigned byte conversion still saturates at 0). Used for 2- and
+// 4-bit unsigned and 8-bit signed codes.
+template <int KB, bool KS>
+__device__ __forceinline__ void key_codes_in_range(const float (&x)[kGroup], float se, float r, float zp,
+                                                   uint32_t (&w)[KB])
+{
+    if constexpr (KS) {
+        uint32_t q[kGroup];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) q[j] = (uint32_t)(int32_t)rintf(quot(x[j], se, r) - zp);
+        pack32<KB>(q, w);
+    } else if constexpr (KB == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t ev = 0, od = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                ev = __builtin_amdgcn_cvt_pk_u8_f32(quot(x[8 * k + 2 * t], se, r) - zp, t, ev);
+                od = __builtin_amdgcn_cvt_pk_u8_f32(quot(x[8 * k + 2 * t + 1], se, r) - zp, t, od);
+            }
+            w[k] = ev | (od << 4);
+        }
+    } else {
+        static_assert(KB == 2, "in-range key codes: 2-bit, 4-bit or signed 8-bit");
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t d4[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    d4[rr] = __builtin_amdgcn_cvt_pk_u8_f32(quot(x[16 * k + 4 * t + rr], se, r) - zp, t, d4[rr]);
+            }
+            w[k] = d4[0] | (d4[1] << 2) | (d4[2] << 4) | (d4[3] << 6);
+        }
+    }
+}
+
+// One key group: scale = (max - min) / maxv (signed: / (2 maxv)), zero point
+// rint(min / (scale + eps)) (signed: rint((max + min) / (2 (scale + eps)))),
+// codes clip(rint(x / (scale + eps) - zero)). The divisions by the constant
+// and by scale + eps are exact quotients from a reciprocal (file header);
+// IEEE division is kept for the reciprocal itself and for groups whose
+// magnitudes leave the range where the quotient is exact. Rounding is
+// monotone in x, so the codes of the group's minimum and maximum bound
+// every element's code: when both are in range the clamp is skipped.
 template <int KB, bool KS>
 __device__ __forceinline__ void key_encode_group(const float (&x)[kGroup], uint8_t *codes,
                                                  uint16_t *scale_out, uint16_t *zero_out)
@@ -606,22 +712,34 @@ __device__ __forceinline__ void key_encode_group(const float (&x)[kGroup], uint8
     group_min_max(x, mn, mx);
     const float eps = 1e-8f;
     constexpr int maxv = KS ? 127 : (1 << KB) - 1;
-    float scale, zp;
-    if constexpr (KS) {
-        scale = (mx - mn) / (float)(2 * maxv);
-        const float denom = 2.0f * (scale + eps);
-        zp = rintf((mx + mn) / denom);
-    } else {
-        scale = (mx - mn) / (float)maxv;
-        zp = rintf(mn / (scale + eps));
-    }
+    constexpr float dv = (float)(KS ? 2 * maxv : maxv);
+    constexpr float rdv = 1.0f / dv; // RN(1/dv), rounded by the compiler
+    const float range = mx - mn;
+    const bool range_ok = range >= 0x1p-100f && range < 0x1p100f; // quotient exact and normal
+    const float scale = range_ok ? quot_signed(range, dv, rdv) : range / dv;
     const float se = scale + eps;
     const float r = 1.0f / se;
     const float amax = fmaxf(fabsf(mn), fabsf(mx));
     const bool fast = (se < 1e30f) && (amax * r < 1e30f);
+    float zp;
+    if constexpr (KS) {
+        const float num = mx + mn;
+        // 2 * se and r / 2 are exact: the quotient by 2 * se from RN(1/(2 se))
+        zp = rintf(fast ? quot_signed(num, 2.0f * se, 0.5f * r) : num / (2.0f * se));
+    } else {
+        zp = rintf(fast ? quot_signed(mn, se, r) : mn / se);
+    }
     uint32_t w[KB];
     if (fast) {
-        key_codes<KB, KS>(x, se, r, zp, w, /*ieee=*/false);
+        constexpr bool has_in_range = KS || KB == 2 || KB == 4;
+        const float hi = rintf(quot(mx, se, r) - zp);
+        const float lo = rintf(quot(mn, se, r) - zp);
+        const bool in_range = KS ? (hi <= (float)maxv && lo >= -(float)maxv) : (hi <= (float)maxv);
+        if (has_in_range && in_range) {
+            if constexpr (has_in_range) key_codes_in_range<KB, KS>(x, se, r, zp, w);
+        } else {
+            key_codes<KB, KS>(x, se, r, zp, w, /*ieee=*/false);
+        }
     } else {
         key_codes<KB, KS>(x, se, r, zp, w, /*ieee=*/true);
     }
@@ -765,15 +883,54 @@ __device__ __forceinline__ void raw_to_f32(const RawGroup<BF16> &r, uint32_t sma
     }
 }
 
+// binary32 values of a raw group, each element's sign flipped by the XOR
+// masks `m` (layout of SignXor)
+template <bool BF16>
+__device__ __forceinline__ void raw_to_f32_xor(const RawGroup<BF16> &r, const uint4 *m, float (&x)[kGroup])
+{
+#pragma unroll
+    for (int i = 0; i < (BF16 ? 4 : 8); ++i) {
+        const uint4 mi = m[i];
+        const uint32_t w[4] = {r.v[i].x ^ mi.x, r.v[i].y ^ mi.y, r.v[i].z ^ mi.z, r.v[i].w ^ mi.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if constexpr (BF16) {
+                const int k = 4 * i + t;
+                x[2 * k] = as_f(w[t] << 16);
+                x[2 * k + 1] = as_f(w[t] & 0xffff0000u);
+            } else {
+                x[4 * i + t] = as_f(w[t]);
+            }
+        }
+    }
+}
+
+// Bins of the 32 values z_j = y_j * r (r = RN(1/(rms + 1e-8)), so
+// |z_j| < 6), packed as they are found: code j at bits [j*B, j*B+B).
+template <int B>
+__device__ __forceinline__ void bin_pack(const float (&y)[kGroup], float r, const BinCell *lut, uint32_t (&w)[B])
+{
+#pragma unroll
+    for (int k = 0; k < B; ++k) w[k] = 0;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+        const uint32_t q = bin_index_bounded<B>(y[j] * r, lut);
+        const int pos = j * B, k = pos >> 5, sh = pos & 31;
+        w[k] |= q << sh;
+        if (sh + B > 32) w[k + 1] |= q >> (32 - sh);
+    }
+}
+
 // Tile loop of the encoder for one key mode (KB = 0: values only): a
 // wavefront walks tiles t, t + stride, ... Loads always read a valid row
 // (rows past the end read the last row, whose results are not stored), so
-// they need no branch.
+// they need no branch. The value side runs first: it is the longer one,
+// and the key group's raw words wait in registers meanwhile.
 template <int D, int VB, int KB, bool KS, bool BF16IN>
 __device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const void *__restrict__ vin, int64_t rows,
                                             uint8_t *__restrict__ kc, uint16_t *__restrict__ ks,
                                             uint16_t *__restrict__ kz, uint8_t *__restrict__ vc,
-                                            uint16_t *__restrict__ vs, const BinCell *lut)
+                                            uint16_t *__restrict__ vs, const BinCell *lut, const uint32_t *sxor)
 {
     constexpr int G = D / kGroup;
     constexpr int RPW = kWave / G;
@@ -782,7 +939,7 @@ __device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); // wavefront-uniform
     const int g = lane % G;
     const int rl = lane / G;
-    const uint32_t smask = dev_sign<D>(g);
+    const uint4 *smask = reinterpret_cast<const uint4 *>(sxor + g * SignXor<D, BF16IN>::W);
     const Rot<D> rot(g);
     const bool hasv = vin != nullptr;
     const int64_t tiles = (rows + RPW - 1) / RPW;
@@ -795,14 +952,9 @@ __device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const 
         RawGroup<BF16IN> kraw, vraw;
         if constexpr (HASK) load_raw<BF16IN>(kin, e0, kraw);
         if (hasv) load_raw<BF16IN>(vin, e0, vraw);
-        if constexpr (HASK) {
-            float x[kGroup];
-            raw_to_f32<BF16IN>(kraw, 0u, x);
-            if (act) key_encode_group<KB, KS>(x, kc + grp * (4 * KB), ks + grp, kz + grp);
-        }
         if (hasv) {
             float y[kGroup];
-            raw_to_f32<BF16IN>(vraw, smask, y);
+            raw_to_f32_xor<BF16IN>(vraw, smask, y);
             hadamard<D>(y, rot);
             float ss = 0.0f;
 #pragma unroll
@@ -812,22 +964,25 @@ __device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const 
             }
             const float s = sqrtf(ss / (float)kGroup);
             const float se = s + 1e-8f;
-            const float r = 1.0f / se;
-            uint32_t q[kGroup];
+            uint32_t w[VB];
             if (se < 1e30f) {
                 // ss finite: every y finite and |y / se| <= sqrt(32)
-#pragma unroll
-                for (int j = 0; j < kGroup; ++j) q[j] = bin_index_bounded<VB>(quot(y[j], se, r), lut);
+                bin_pack<VB>(y, 1.0f / se, lut, w);
             } else {
+                uint32_t q[kGroup];
 #pragma unroll
                 for (int j = 0; j < kGroup; ++j) q[j] = bin_index_any<VB>(y[j] / se, lut);
+                pack32<VB>(q, w);
             }
             if (act) {
-                uint32_t w[VB];
-                pack32<VB>(q, w);
                 store_codes<VB>(vc + grp * (4 * VB), w);
                 vs[grp] = f32_to_f16_bits(s);
             }
+        }
+        if constexpr (HASK) {
+            float x[kGroup];
+            raw_to_f32<BF16IN>(kraw, 0u, x);
+            if (act) key_encode_group<KB, KS>(x, kc + grp * (4 * KB), ks + grp, kz + grp);
         }
     }
 }
@@ -845,20 +1000,24 @@ encode_kernel(const void *__restrict__ kin, const void *__restrict__ vin, int64_
               uint8_t *__restrict__ vc, uint16_t *__restrict__ vs)
 {
     constexpr int NCELL = BinGrid<VB>::N;
+    constexpr int NSX = (D / kGroup) * SignXor<D, BF16IN>::W;
     __shared__ BinCell lut[NCELL];
+    __shared__ __attribute__((aligned(16))) uint32_t sxor[NSX];
     if (vin != nullptr) {
         const BinCell *src = dev_lut<VB>();
         for (int i = threadIdx.x; i < NCELL; i += kBlockThreads) lut[i] = src[i];
+        const uint32_t *sx = dev_sign_xor<D, BF16IN>();
+        for (int i = threadIdx.x; i < NSX; i += kBlockThreads) sxor[i] = sx[i];
         __syncthreads();
     }
     switch (kmode) {
-    case 2: encode_loop<D, VB, 2, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
-    case 3: encode_loop<D, VB, 3, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
-    case 4: encode_loop<D, VB, 4, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
-    case 5: encode_loop<D, VB, 5, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
-    case 8: encode_loop<D, VB, 8, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
-    case 8 | 16: encode_loop<D, VB, 8, true, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
-    default: encode_loop<D, VB, 0, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut); break;
+    case 2: encode_loop<D, VB, 2, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut, sxor); break;
+    case 3: encode_loop<D, VB, 3, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut, sxor); break;
+    case 4: encode_loop<D, VB, 4, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut, sxor); break;
+    case 5: encode_loop<D, VB, 5, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut, sxor); break;
+    case 8: encode_loop<D, VB, 8, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut, sxor); break;
+    case 8 | 16: encode_loop<D, VB, 8, true, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut, sxor); break;
+    default: encode_loop<D, VB, 0, false, BF16IN>(kin, vin, rows, kc, ks, kz, vc, vs, lut, sxor); break;
     }
 }
 

@@ -17,6 +17,7 @@ codec library and torch use).
 from __future__ import annotations
 
 import ctypes
+import gc
 
 _P = ctypes.c_void_p
 _hip = None
@@ -92,12 +93,27 @@ class HipGraph:
         self.stream = s.value
         self.graph, self.exec = _P(), _P()
         torch.cuda.synchronize()
-        _check(L.hipStreamBeginCapture(self.stream, HIP_STREAM_CAPTURE_MODE_GLOBAL), "hipStreamBeginCapture")
+        # No garbage collection while capturing: a collected object's
+        # destructor may call the HIP runtime (free memory, destroy an event
+        # or a graph), which a global-mode capture forbids and the runtime
+        # answers by aborting the process.
+        gc.collect()
+        gc_was_on = gc.isenabled()
+        gc.disable()
         try:
-            with torch.cuda.stream(torch.cuda.ExternalStream(self.stream)):
-                record()
-        finally:
+            _check(L.hipStreamBeginCapture(self.stream, HIP_STREAM_CAPTURE_MODE_GLOBAL), "hipStreamBeginCapture")
+            try:
+                with torch.cuda.stream(torch.cuda.ExternalStream(self.stream)):
+                    record()
+            except BaseException:
+                # end the capture, drop what it recorded, and report the caller's error
+                L.hipStreamEndCapture(self.stream, ctypes.byref(self.graph))
+                self.close()
+                raise
             _check(L.hipStreamEndCapture(self.stream, ctypes.byref(self.graph)), "hipStreamEndCapture")
+        finally:
+            if gc_was_on:
+                gc.enable()
         _check(L.hipGraphInstantiate(ctypes.byref(self.exec), self.graph, None, None, 0), "hipGraphInstantiate")
 
     def launch(self):

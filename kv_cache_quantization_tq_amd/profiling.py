@@ -6,7 +6,9 @@
 
 ``trace`` prints per-kernel dispatch counts and average / median / 10th
 and 90th percentile / min durations from a ``--kernel-trace`` CSV, and with ``--stats`` the codec
-kernels' rows of rocprofv3's own ``--stats`` table. ``traffic`` turns the FETCH_SIZE and
+kernels' rows of rocprofv3's own ``--stats`` table; ``--json`` also writes the per-kind figures
+with the SHA-256 of each kind's sources (bench.py reports them beside its own timing when the
+sources still match). ``traffic`` turns the FETCH_SIZE and
 WRITE_SIZE counters (KiB per dispatch) of two ``--pmc`` runs of
 ``bench.py --copy-calibration-mib N`` into HBM bytes per launch: each
 counter is scaled by the factor that maps the same counter, read on the
@@ -87,6 +89,27 @@ def trace_summary(path: str, ops: dict | None = None) -> str:
     return "\n".join(lines)
 
 
+def trace_kinds(path: str, ops: dict | None = None) -> dict:
+    """Per kernel kind: dispatches and average / median / 10th and 90th
+    percentile duration (us) over the trace, with the SHA-256 of that kind's
+    sources; with ops[kind] = N, also the kernel time per operation (one
+    operation being several launches)."""
+    from kv_cache_quantization_tq_amd.build import source_digest
+    tr = read_trace(path)
+    res = {}
+    for kind in KINDS:
+        d = [v for name, vs in tr.items() if kernel_kind(name) == kind for v in vs]
+        if not d:
+            continue
+        res[kind] = {"dispatches": len(d), "avg_us": sum(d) / len(d), "median_us": statistics.median(d),
+                     "p10_us": percentile(d, 10), "p90_us": percentile(d, 90), "min_us": min(d),
+                     "source_sha256": source_digest(kind)}
+        if ops and kind in ops:
+            res[kind]["operations"] = ops[kind]
+            res[kind]["per_operation_us"] = sum(d) / ops[kind]
+    return res
+
+
 def stats_summary(path: str) -> str:
     lines = [f"{'kernel (rocprofv3 --stats)':70s} {'calls':>5s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s}"]
     with open(path) as f:
@@ -151,6 +174,7 @@ def main(argv=None):
     t.add_argument("csv")
     t.add_argument("--stats")
     t.add_argument("--ops", action="append", default=[], help="KIND=N: also report kernel time per operation")
+    t.add_argument("--json", help="also write per-kind figures (with source digests) to this file")
     c = sub.add_parser("traffic")
     c.add_argument("fetch_csv")
     c.add_argument("write_csv")
@@ -160,7 +184,11 @@ def main(argv=None):
                    help="KIND=N: that kind's launches form N operations; report bytes per operation")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace_summary(a.csv, {k: int(v) for k, v in (o.split("=") for o in a.ops)}))
+        ops = {k: int(v) for k, v in (o.split("=") for o in a.ops)}
+        print(trace_summary(a.csv, ops))
+        if a.json:
+            with open(a.json, "w") as f:
+                f.write(json.dumps(trace_kinds(a.csv, ops), indent=1) + "\n")
         if a.stats:
             print()
             print(stats_summary(a.stats))

@@ -20,6 +20,11 @@ model K/V caches:
                   from fp32 N(0,1); each step appends one token per head
                   (fp32 N(0,1)) and decodes the whole cache to bf16; values
                   5-bit, keys 4-bit.
+* ``long_k8v3``   batch 1, 8 KV heads, head_dim 256, 32768 tokens from fp32
+                  N(0,1); values 3-bit, keys 8-bit signed: the ops page's
+                  specialised long-sequence decode configuration
+                  (tryDecodePackedKv: head_dim 256, 8-bit keys, 3-bit values,
+                  at least 8192 tokens).
 * ``joint_large`` batch 4 x 65536 tokens, 8 KV heads, head_dim 512, bf16
                   N(0,1) with 1% of the (token, head) rows zeroed (the same
                   rows in K and V); values 8-bit (one byte per code), keys
@@ -72,6 +77,7 @@ WORKLOADS = {
     "small_head": Workload("small_head", 16, 4096, 4, 64, "bf16", 2, 8, True, 2, "student_t_outliers"),
     "long_decode": Workload("long_decode", 1, 131072, 8, 256, "f32", 5, 4, False, 3, "gauss"),
     "joint_large": Workload("joint_large", 4, 65536, 8, 512, "bf16", 8, 4, False, 4, "gauss_zero_rows"),
+    "long_k8v3": Workload("long_k8v3", 1, 32768, 8, 256, "f32", 3, 8, True, 8, "gauss"),
 }
 
 

@@ -108,3 +108,35 @@ def rows_as_f32(x: np.ndarray) -> np.ndarray:
     if x.dtype == np.uint16:
         x = (x.astype(np.uint32) << 16).view(np.float32)
     return x.reshape(-1, x.shape[-1])
+
+
+# ---------------------------------------------------------------- full size
+
+def oracle_threads() -> int:
+    """Threads for the oracle over row ranges (its C calls release the GIL);
+    at most 16, the host share of one GPU."""
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _row_split(n: int, parts: int):
+    cuts = [n * i // parts for i in range(parts + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(parts) if cuts[i + 1] > cuts[i]]
+
+
+def oracle_encode_threaded(kn, vn, **cfg) -> dict:
+    """O.encode_kv over row ranges in threads, planes concatenated in row order."""
+    import concurrent.futures as cf
+    parts = _row_split(kn.shape[0], oracle_threads())
+    with cf.ThreadPoolExecutor(len(parts)) as ex:
+        outs = list(ex.map(lambda ab: O.encode_kv(kn[ab[0]:ab[1]], vn[ab[0]:ab[1]], **cfg), parts))
+    return {n: np.concatenate([o[n] for o in outs]) for n in outs[0]}
+
+
+def oracle_decode_threaded(planes: dict, rows: int, **cfg):
+    import concurrent.futures as cf
+    parts = _row_split(rows, oracle_threads())
+    with cf.ThreadPoolExecutor(len(parts)) as ex:
+        outs = list(ex.map(lambda ab: O.decode_kv({n: p[ab[0]:ab[1]] for n, p in planes.items()},
+                                                    rows=ab[1] - ab[0], **cfg), parts))
+    return np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs])

@@ -49,8 +49,9 @@ def test_packed_dim():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert isinstance(tq.status_string(s), str) and tq.status_string(s)
+        assert tq.status_string(s) != "unknown status"
     assert tq.status_string(99) == "unknown status"
 
 
@@ -159,6 +160,47 @@ def test_kernel_bin_search_equals_oracle_count(bits):
     z = np.concatenate(z)
     z = z[~np.isnan(z)]
     np.testing.assert_array_equal(tq.value_bin_host(bits, z), O.bin_index(z, bits))
+
+
+def test_kernel_quotient_equals_ieee_division():
+    """The quotient the kernels take for key scales, zero points and codes
+    (host build of the same code) equals IEEE binary32 division bit for bit,
+    the sign of zero included, over the range where the kernels use it
+    (divisor in [1e-8, 1e30), |a * RN(1/b)| < 1e30, quotient not subnormal):
+    random operands over wide exponents, the constant divisors of the key
+    scales, divisors one ulp around powers of two, and signed zeros."""
+    rng = np.random.default_rng(77)
+    n = 400000
+
+    def wide(k, lo, hi):
+        m = rng.uniform(1.0, 2.0, k)
+        e = rng.integers(lo, hi, k)
+        return (np.ldexp(m, e) * rng.choice([-1.0, 1.0], k)).astype(np.float32)
+
+    a = [wide(n, -60, 60), np.zeros(1000, np.float32), -np.zeros(1000, np.float32)]
+    b = [np.abs(wide(n, -26, 99)), np.abs(wide(2000, -20, 20))]
+    a = np.concatenate(a)
+    b = np.concatenate([np.resize(np.concatenate(b), a.size)])
+    # constant divisors of the key scales and divisors next to powers of two
+    consts = np.array([3, 7, 15, 31, 255, 254], np.float32)
+    p2 = np.ldexp(np.ones(80), np.arange(-26, 54)).astype(np.float32)
+    near = np.concatenate([p2, np.nextafter(p2, np.float32(0)), np.nextafter(p2, np.float32(np.inf))])
+    hard_b = np.concatenate([consts, near])
+    hard_a = wide(hard_b.size * 64, -20, 20)
+    a = np.concatenate([a, hard_a, np.nextafter(hard_a, np.float32(0))])
+    b = np.concatenate([b, np.repeat(hard_b, 64), np.repeat(hard_b, 64)])
+    r = (np.float32(1.0) / b).astype(np.float32)
+    with np.errstate(over="ignore", under="ignore"):
+        want = (a / b).astype(np.float32)
+        ar = np.abs(a.astype(np.float64) * r.astype(np.float64))
+    keep = (b >= np.float32(1e-8)) & (b < np.float32(1e30)) & (ar < 1e30) & \
+        ((np.abs(want) >= np.float32(2.0 ** -126)) | (a == 0))
+    a, b, want = a[keep], b[keep], want[keep]
+    assert a.size > 300000
+    got = tq.quotient_host(a, b)
+    bad = got.view(np.uint32) != want.view(np.uint32)
+    assert not bad.any(), (int(bad.sum()), a[bad][:3], b[bad][:3])
+    assert np.signbit(got[a == 0]).sum() == np.signbit(a[a == 0]).sum() > 0
 
 
 def _pk(vals):

@@ -10,6 +10,8 @@ output must equal the eager result bit for bit.
 """
 from __future__ import annotations
 
+import gc
+
 import pytest
 import torch
 
@@ -42,9 +44,16 @@ class Captured:
     def __init__(self, how, record):
         self.how = how
         if how == "torch":
-            self.g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(self.g):
-                record()
+            # no garbage collection during the capture (a destructor calling
+            # the HIP runtime there would abort the process)
+            gc.collect()
+            gc.disable()
+            try:
+                self.g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(self.g):
+                    record()
+            finally:
+                gc.enable()
         else:
             self.g = HipGraph(torch, record)
         torch.cuda.synchronize()
@@ -158,3 +167,45 @@ def test_merge_graph_replays(how):
         tq.merge_rows(other, lens, heads=H, head_dim=d, k_bits=kb, v_bits=vb)
 
     check_replays(graph, [dst[n] for n in ref], {f"merged {n}": p for n, p in ref.items()}, between)
+
+
+def many_caches(n, H, d, kb, vb, seed):
+    lens = [37 + 11 * i for i in range(n)]
+    return lens, [W.random_planes(m, H, d, kb, vb, seed=seed + i, device=DEV) for i, m in enumerate(lens)]
+
+
+@pytest.mark.parametrize("how", HOW)
+def test_multi_launch_merge_refuses_capture(how):
+    """A merge needing more than one launch (30 caches: 300 plane segments,
+    120 per launch) returns TQ_E_CAPTURE while its stream captures, having
+    launched nothing; launched directly it still works."""
+    H, d, kb, vb = 2, 64, 4, 4
+    lens, caches = many_caches(30, H, d, kb, vb, seed=61)
+    dst = tq.empty_planes(len(lens) * max(lens) * H, d, kb, vb, DEV)
+    for p in dst.values():
+        p.fill_(0x5A if p.dtype == torch.uint8 else 0x5A5A)
+    torch.cuda.synchronize()
+    before = {n: p.clone() for n, p in dst.items()}
+    with pytest.raises(tq.TQError) as err:
+        Captured(how, lambda: tq.merge_rows(caches, lens, heads=H, head_dim=d, k_bits=kb, v_bits=vb, out=dst))
+    assert err.value.status == tq.TQ_E_CAPTURE
+    torch.cuda.synchronize()
+    for n in dst:
+        assert torch.equal(dst[n], before[n]), f"plane {n} written by a refused call"
+    ref, _, _ = tq.merge_rows(caches, lens, heads=H, head_dim=d, k_bits=kb, v_bits=vb)
+    torch.cuda.synchronize()
+    assert all(p.numel() > 0 for p in ref.values())
+
+
+@pytest.mark.skip(reason="a graph replay of 20 captured 32-cache merges (three launches each, 2.9 KB segment "
+                         "lists as kernel arguments) faulted the GPU once and no cause has been shown in this "
+                         "library's code; such calls now refuse capture (TQ_E_CAPTURE) and this case stays "
+                         "off the GPU")
+def test_multi_launch_merge_graph_replays():
+    H, d, kb, vb = 8, 128, 4, 4
+    lens, caches = many_caches(32, H, d, kb, vb, seed=71)
+    dst = tq.empty_planes(len(lens) * max(lens) * H, d, kb, vb, DEV)
+    graph = Captured("hip", lambda: [tq.merge_rows(caches, lens, heads=H, head_dim=d, k_bits=kb, v_bits=vb,
+                                                   out=dst) for _ in range(20)])
+    graph.replay()
+    graph.close()

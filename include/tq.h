@@ -66,8 +66,10 @@ enum {
     TQ_E_DTYPE = 5,    /* dtype not TQ_F32 / TQ_BF16                          */
     TQ_E_SHAPE = 6,    /* negative tokens, heads < 1, or row count overflow   */
     TQ_E_HIP = 7,      /* the HIP runtime reported an error at launch         */
-    TQ_E_CAPTURE = 8   /* a batching call needing more than one launch was    */
+    TQ_E_CAPTURE = 8,  /* a batching call needing more than one launch was    */
                        /* made on a stream that is capturing a graph          */
+    TQ_E_SCRATCH = 9   /* the call needs more scratch than the library's      */
+                       /* static buffer holds                                 */
 };
 
 /* Element types of K/V inputs and decoded outputs. */
@@ -256,6 +258,20 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
                             const int32_t *left_pad, int32_t kv_heads, int32_t q_heads, const tq_config *cfg,
                             float scale, void *out, int32_t out_dtype, void *workspace, int64_t workspace_bytes,
                             void *stream);
+
+/* tq_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under graph capture, serving loops
+ * that forbid allocation). The split partials go to a static buffer of 64
+ * MiB in the library's device image, one per GPU, held until the process
+ * ends; this call allocates nothing. Arguments, results and errors are
+ * those of tq_attention_decode, plus TQ_E_SCRATCH (returned before any
+ * launch) when tq_attention_workspace_bytes() for the call exceeds 64 MiB.
+ * All calls on one GPU share its buffer and each call leaves its partials
+ * there: calls that may overlap on one GPU (concurrent streams, or host
+ * threads) race and must be ordered by the caller. */
+int32_t tq_attention_decode_static(const void *q, int32_t q_dtype, const tq_packed_kv *cache, int32_t batch,
+                                   int64_t width, const int32_t *left_pad, int32_t kv_heads, int32_t q_heads,
+                                   const tq_config *cfg, float scale, void *out, int32_t out_dtype, void *stream);
 
 /* ---------------------------------------------------------------------
  * Lloyd-Max table fitting (page "mlx-bun 0.0.9 -> 0.0.11",

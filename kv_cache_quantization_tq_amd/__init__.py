@@ -29,7 +29,8 @@ HEAD_DIMS = (64, 128, 256, 512)
 VALUE_BITS = (2, 3, 4, 5, 8)
 KEY_BITS = (2, 3, 4, 5, 8)
 
-TQ_OK, TQ_E_NULL, TQ_E_HEAD_DIM, TQ_E_BITS, TQ_E_ALIGN, TQ_E_DTYPE, TQ_E_SHAPE, TQ_E_HIP, TQ_E_CAPTURE = range(9)
+TQ_OK, TQ_E_NULL, TQ_E_HEAD_DIM, TQ_E_BITS, TQ_E_ALIGN, TQ_E_DTYPE, TQ_E_SHAPE, TQ_E_HIP, TQ_E_CAPTURE, \
+    TQ_E_SCRATCH = range(10)
 TQ_F32, TQ_BF16 = 0, 1
 TQ_DECODE_ROTATED_V = 1
 
@@ -39,7 +40,7 @@ EXPORTS = (
     "tq_lloyd_max_table", "tq_sign_vector", "tq_value_bin_host", "tq_quotient_host",
     "tq_merge_rows", "tq_extend_rows", "tq_extract_row", "tq_filter_rows",
     "tq_lloyd_max_workspace_bytes", "tq_lloyd_max_fit",
-    "tq_attention_workspace_bytes", "tq_attention_decode",
+    "tq_attention_workspace_bytes", "tq_attention_decode", "tq_attention_decode_static",
 )
 
 
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
             "tq_attention_workspace_bytes": (i64, [i32, i32, i32, i32, i64]),
             "tq_attention_decode": (i32, [P, i32, ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
                                           ctypes.POINTER(TQConfig), ctypes.c_float, P, i32, P, i64, P]),
+            "tq_attention_decode_static": (i32, [P, i32, ctypes.POINTER(TQPackedKV), i32, i64, P, i32, i32,
+                                                 ctypes.POINTER(TQConfig), ctypes.c_float, P, i32, P]),
             "tq_lloyd_max_fit": (i32, [P, i64, i32, P, i32, P, P, P, i64, P]),
         }
         for name, (res, args) in sig.items():
@@ -422,4 +425,28 @@ def attention_decode(q, cache, *, batch: int, width: int, kv_heads: int, head_di
                                    _stream_handle(stream))
     if st:
         raise TQError(st, "tq_attention_decode")
+    return out
+
+
+def attention_decode_static(q, cache, *, batch: int, width: int, kv_heads: int, head_dim: int, k_bits: int,
+                            v_bits: int, k_signed: bool = False, left_pad=None, scale: Optional[float] = None,
+                            out=None, stream=None):
+    """attention_decode through tq_attention_decode_static: no workspace,
+    the split partials go to the library's static per-GPU buffer. `out`
+    must be given (this path allocates nothing)."""
+    import math
+    if out is None:
+        raise ValueError("attention_decode_static needs `out` (it allocates nothing)")
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous")
+    torch = _torch()
+    if left_pad is not None and (left_pad.dtype != torch.int32 or not left_pad.is_cuda):
+        raise ValueError("left_pad must be a device int32 tensor")
+    cfg = TQConfig(head_dim, k_bits, v_bits, int(bool(k_signed)))
+    sc = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+    st = lib().tq_attention_decode_static(_ptr(q), _dtype_code(q), ctypes.byref(_packed(cache)), batch, width,
+                                          _ptr(left_pad), kv_heads, q.shape[1], ctypes.byref(cfg), sc, _ptr(out),
+                                          _dtype_code(out), _stream_handle(stream))
+    if st:
+        raise TQError(st, "tq_attention_decode_static")
     return out

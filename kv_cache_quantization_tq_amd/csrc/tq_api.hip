@@ -135,6 +135,7 @@ const char *tq_status_string(int32_t status)
     case TQ_E_SHAPE: return "tokens must be >= 0 and heads >= 1 (row count within range)";
     case TQ_E_HIP: return "HIP runtime error at kernel launch";
     case TQ_E_CAPTURE: return "batching call needs more than one launch and its stream is capturing a graph";
+    case TQ_E_SCRATCH: return "the call needs more scratch than the library's static buffer (64 MiB) holds";
     default: return "unknown status";
     }
 }

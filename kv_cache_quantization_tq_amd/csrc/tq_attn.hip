@@ -630,6 +630,67 @@ int64_t wave_tokens(int64_t width, int64_t nsplit)
     return nsplit > 0 ? (width + nsplit * kWavesPerBlock - 1) / (nsplit * kWavesPerBlock) : 0;
 }
 
+// Split partials of tq_attention_decode_static, for callers that cannot
+// allocate: a fixed array in the library's device image (each GPU the
+// library runs on holds its own copy until the process ends). Host code
+// must not pass `scratch` itself to a kernel (on the host the name is a
+// stand-in, not a device address): it uses the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr int64_t kAttnScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per
+// device; nullptr if the runtime reports an error.
+void *scratch_address()
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev] = ptr;
+    }
+    return addr[dev];
+}
+
+// Every argument check of tq_attention_decode except those of the
+// workspace, in the order the pages' operations would throw.
+int32_t attention_args_status(const void *q, int32_t q_dtype, const tq_packed_kv *cache, int32_t batch,
+                              int64_t width, int32_t kv_heads, int32_t q_heads, const tq_config *cfg, float scale,
+                              const void *out, int32_t out_dtype)
+{
+    if (cfg == nullptr || cache == nullptr) return TQ_E_NULL;
+    if (!tq_host::valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
+    if (!tq_host::valid_key_cfg(cfg) || !tq_host::valid_bits(cfg->v_bits)) return TQ_E_BITS;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_E_DTYPE;
+    if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_E_DTYPE;
+    if (batch < 0 || width < 0 || width > ((int64_t)1 << 40) || kv_heads < 1 || q_heads < kv_heads ||
+        q_heads % kv_heads != 0 || q_heads / kv_heads > kAttnMaxG || !(scale == scale))
+        return TQ_E_SHAPE;
+    if (((q_heads / kv_heads) & (q_heads / kv_heads - 1)) != 0) // 1, 2, 4 or 8 query heads per KV head
+        return TQ_E_SHAPE;
+    if ((int64_t)batch * width * kv_heads > ((int64_t)1 << 40)) return TQ_E_SHAPE;
+    if ((int64_t)batch * q_heads > 0x7fffffff) return TQ_E_SHAPE; // one combine block per output row
+    if (batch == 0) return TQ_OK;
+    if (q == nullptr || out == nullptr) return TQ_E_NULL;
+    if (!tq_host::aligned(q, 16) || !tq_host::aligned(out, 16)) return TQ_E_ALIGN;
+    if (width > 0) {
+        if (cache->k_codes == nullptr || cache->k_scale == nullptr || cache->k_zero == nullptr ||
+            cache->v_codes == nullptr || cache->v_scale == nullptr)
+            return TQ_E_NULL;
+        if (!tq_host::aligned(cache->k_codes, tq_host::code_align(cfg->k_bits)) ||
+            !tq_host::aligned(cache->v_codes, tq_host::code_align(cfg->v_bits)) ||
+            !tq_host::aligned(cache->k_scale, 8) || !tq_host::aligned(cache->k_zero, 8) ||
+            !tq_host::aligned(cache->v_scale, 8))
+            return TQ_E_ALIGN;
+    }
+    return TQ_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -650,36 +711,16 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
                             float scale, void *out, int32_t out_dtype, void *workspace, int64_t workspace_bytes,
                             void *stream)
 {
-    if (cfg == nullptr || cache == nullptr) return TQ_E_NULL;
-    if (!tq_host::valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
-    if (!tq_host::valid_key_cfg(cfg) || !tq_host::valid_bits(cfg->v_bits)) return TQ_E_BITS;
-    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_E_DTYPE;
-    if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_E_DTYPE;
-    if (batch < 0 || width < 0 || width > ((int64_t)1 << 40) || kv_heads < 1 || q_heads < kv_heads ||
-        q_heads % kv_heads != 0 || q_heads / kv_heads > kAttnMaxG || !(scale == scale))
-        return TQ_E_SHAPE;
-    if (((q_heads / kv_heads) & (q_heads / kv_heads - 1)) != 0) // 1, 2, 4 or 8 query heads per KV head
-        return TQ_E_SHAPE;
-    if ((int64_t)batch * width * kv_heads > ((int64_t)1 << 40)) return TQ_E_SHAPE;
-    if ((int64_t)batch * q_heads > 0x7fffffff) return TQ_E_SHAPE; // one combine block per output row
-
+    const int32_t st = attention_args_status(q, q_dtype, cache, batch, width, kv_heads, q_heads, cfg, scale, out,
+                                             out_dtype);
+    if (st != TQ_OK) return st;
     if (batch == 0) return TQ_OK;
     const int32_t d = cfg->head_dim;
-    if (q == nullptr || out == nullptr) return TQ_E_NULL;
-    if (!tq_host::aligned(q, 16) || !tq_host::aligned(out, 16)) return TQ_E_ALIGN;
     int64_t nch = 0;
     if (width > 0) {
         if (workspace == nullptr) return TQ_E_NULL;
         if (workspace_bytes < tq_attention_workspace_bytes(batch, kv_heads, q_heads, d, width)) return TQ_E_SHAPE;
         if (!tq_host::aligned(workspace, 16)) return TQ_E_ALIGN;
-        if (cache->k_codes == nullptr || cache->k_scale == nullptr || cache->k_zero == nullptr ||
-            cache->v_codes == nullptr || cache->v_scale == nullptr)
-            return TQ_E_NULL;
-        if (!tq_host::aligned(cache->k_codes, tq_host::code_align(cfg->k_bits)) ||
-            !tq_host::aligned(cache->v_codes, tq_host::code_align(cfg->v_bits)) ||
-            !tq_host::aligned(cache->k_scale, 8) || !tq_host::aligned(cache->k_zero, 8) ||
-            !tq_host::aligned(cache->v_scale, 8))
-            return TQ_E_ALIGN;
         AttnParams p;
         p.q = q;
         p.kc = static_cast<const uint8_t *>(cache->k_codes);
@@ -739,6 +780,24 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
     if (hipLaunchKernel(fn2, dim3((uint32_t)rows), dim3(kBlockThreads), args2, 0, (hipStream_t)stream) != hipSuccess)
         return TQ_E_HIP;
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
+}
+
+int32_t tq_attention_decode_static(const void *q, int32_t q_dtype, const tq_packed_kv *cache, int32_t batch,
+                                   int64_t width, const int32_t *left_pad, int32_t kv_heads, int32_t q_heads,
+                                   const tq_config *cfg, float scale, void *out, int32_t out_dtype, void *stream)
+{
+    if (cfg == nullptr) return TQ_E_NULL;
+    if (!tq_host::valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
+    const int64_t need = tq_attention_workspace_bytes(batch, kv_heads, q_heads, cfg->head_dim, width);
+    if (need < 0) return (int32_t)-need;
+    if (need > kAttnScratchBytes) return TQ_E_SCRATCH;
+    const int32_t st = attention_args_status(q, q_dtype, cache, batch, width, kv_heads, q_heads, cfg, scale, out,
+                                             out_dtype);
+    if (st != TQ_OK) return st;
+    void *ws = nullptr;
+    if (need > 0 && (ws = scratch_address()) == nullptr) return TQ_E_HIP;
+    return tq_attention_decode(q, q_dtype, cache, batch, width, left_pad, kv_heads, q_heads, cfg, scale, out,
+                               out_dtype, ws, kAttnScratchBytes, stream);
 }
 
 } // extern "C"

@@ -49,7 +49,7 @@ def test_packed_dim():
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert isinstance(tq.status_string(s), str) and tq.status_string(s)
         assert tq.status_string(s) != "unknown status"
     assert tq.status_string(99) == "unknown status"
@@ -305,3 +305,24 @@ def test_attention_argument_validation():
     assert call(out=FAKE + 8) == tq.TQ_E_ALIGN
     assert L.tq_attention_decode(FAKE, 0, by(_pk([FAKE, FAKE, None, FAKE, FAKE])), 2, 1000, None, 2, 8, by(cfg),
                                  0.1, FAKE, 0, FAKE, ws, None) == tq.TQ_E_NULL
+
+
+def test_static_attention_rejects_calls_beyond_its_buffer():
+    """tq_attention_decode_static refuses, before any launch or pointer use,
+    a call whose split partials would not fit its 64 MiB static buffer, and
+    reports argument errors as tq_attention_decode does."""
+    L = tq.lib()
+    cfg = tq.TQConfig(512, 4, 4, 0)
+    need = L.tq_attention_workspace_bytes(4096, 8, 64, 512, 64)
+    assert need > 64 << 20
+    st = L.tq_attention_decode_static(None, tq.TQ_BF16, None, 4096, 64, None, 8, 64, ctypes.byref(cfg), 0.1,
+                                      None, tq.TQ_F32, None)
+    assert st == tq.TQ_E_SCRATCH
+    assert L.tq_attention_decode_static(None, tq.TQ_BF16, None, 1, 64, None, 8, 64, None, 0.1, None, tq.TQ_F32,
+                                        None) == tq.TQ_E_NULL
+    bad = tq.TQConfig(96, 4, 4, 0)
+    assert L.tq_attention_decode_static(None, tq.TQ_BF16, None, 1, 64, None, 8, 64, ctypes.byref(bad), 0.1, None,
+                                        tq.TQ_F32, None) == tq.TQ_E_HEAD_DIM
+    # a fitting call with a missing pointer fails its argument check
+    assert L.tq_attention_decode_static(None, tq.TQ_BF16, None, 1, 64, None, 8, 64, ctypes.byref(cfg), 0.1, None,
+                                        tq.TQ_F32, None) == tq.TQ_E_NULL

@@ -22,7 +22,8 @@ import os
 from typing import Dict, Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# the in-tree build; TQ_LIBRARY may name another build of the same sources
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(_HERE, "libtq.so")
 
 BLOCK = 32
 HEAD_DIMS = (64, 128, 256, 512)

@@ -217,10 +217,17 @@ template <int B> __device__ __forceinline__ void codes8(const uint32_t (&w)[B], 
 }
 
 // decodeKeys ((q + zero) * scale, rounded to bf16) of elements 8 c .. 8 c + 7
-// of the quarter, as packed bf16 pairs
-template <int D, int KB, bool KS>
+// of the quarter, as packed bf16 pairs. FMA: as fma(q, scale, zero * scale)
+// (zs = zero * scale), used when every group of the wavefront's tile has a
+// finite nonzero scale and a finite zero point: a code has at most 8
+// significant bits and an fp16 scale or zero at most 11, so both products
+// are exact in binary32, q + zero is an exact integer, and the fma's single
+// rounding is that of (q + zero) * scale. Otherwise the two-step form (which
+// also fixes the sign of a zero result).
+template <int D, int KB, bool KS, bool FMA>
 __device__ __forceinline__ u32x4_t key_chunk(const Quarter<D, KB> &k, int c, const float (&sc)[Quarter<D, KB>::NG],
-                                             const float (&zr)[Quarter<D, KB>::NG])
+                                             const float (&zr)[Quarter<D, KB>::NG],
+                                             const float (&zs)[Quarter<D, KB>::NG])
 {
     const int gi = Quarter<D, KB>::NG > 1 ? 8 * c / kGroup : 0;
     uint32_t q[8];
@@ -233,7 +240,7 @@ __device__ __forceinline__ u32x4_t key_chunk(const Quarter<D, KB> &k, int c, con
         for (int u = 0; u < 2; ++u) {
             const uint32_t x = q[2 * w + u];
             const float qf = KS ? (float)(int32_t)(int8_t)(uint8_t)x : (float)x;
-            f[u] = (qf + zr[gi]) * sc[gi];
+            f[u] = FMA ? __builtin_fmaf(qf, sc[gi], zs[gi]) : (qf + zr[gi]) * sc[gi];
         }
         r[w] = pack_bf16x2(f[0], f[1]);
     }
@@ -310,18 +317,24 @@ __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, in
                                    tk * vstride + vq_off, tk * sstride + vs_off, g, vq);
 
         // scores of the tile's 16 tokens; values into the LDS tile
-        float ksc[KQ::NG], kzr[KQ::NG], vsc[VQ::NG];
+        float ksc[KQ::NG], kzr[KQ::NG], kzs[KQ::NG], vsc[VQ::NG];
+        bool fma_ok = true;
 #pragma unroll
         for (int gi = 0; gi < KQ::NG; ++gi) {
             ksc[gi] = f16_bits_to_f32(kq.scale(gi));
             kzr[gi] = f16_bits_to_f32(kq.zero(gi));
+            kzs[gi] = kzr[gi] * ksc[gi];
+            fma_ok = fma_ok && ksc[gi] != 0.0f && __builtin_isfinite(kzs[gi]);
         }
+        const bool tile_fma = __all(fma_ok);
 #pragma unroll
         for (int gi = 0; gi < VQ::NG; ++gi) vsc[gi] = f16_bits_to_f32(vq.scale(gi));
         f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, key_chunk<D, KB, KS>(kq, cc, ksc, kzr));
+            u32x4_t kc = key_chunk<D, KB, KS, true>(kq, cc, ksc, kzr, kzs);
+            if (!tile_fma) kc = key_chunk<D, KB, KS, false>(kq, cc, ksc, kzr, kzs); // wavefront-uniform, rare
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, kc);
 #pragma unroll
             for (int t = 0; t < QT; ++t) {
                 const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(qrow + t * (kQRows * QR) + 8 * cc);

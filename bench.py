@@ -80,8 +80,8 @@ DESCRIPTION = {
                   "query heads un-rotated (unrotateValues); the eager decode is timed alongside",
     "batch_merge": "batch_merge: 32 packed caches (8 KV heads, head_dim 128, V4/K4 planes of seeded random "
                    "bytes) of 4096..32768 tokens merged into one left-padded batch",
-    "lloyd_fit": "lloyd_fit: 4-bit (16-level) Lloyd-Max table fitted to 2^24 N(0,1) float32 samples, 500 "
-                 "iterations from the printed table",
+    "lloyd_fit": "lloyd_fit: 4-bit (16-level) Lloyd-Max table fitted to 2^24 N(0,1) float32 samples (numpy "
+                 "PCG64 seed 6, drawn on the host), 500 iterations from the printed table",
     "attn_decode": "attn_decode: one query token (32 heads, bf16) attending over the long_decode cache (131072 "
                    "tokens x 8 KV heads, head_dim 256, V5/K4 packed), decoded inside the attention kernel",
 }
@@ -153,6 +153,8 @@ def committed_trace(workload, kernel):
     k = t.get(kernel)
     if not k or k.get("source_sha256") != source_digest(kernel):
         return None
+    if "per_operation_us" in k:  # an operation of several launches: time per operation
+        return {**k, "avg_us": k["per_operation_us"], "p10_us": None, "p90_us": None}
     return k
 
 
@@ -530,10 +532,9 @@ def setup_batch_merge(torch, tq, W, dev):
 def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
     """One full fit per step: the samples are sorted once, then every
     iteration searches the sorted keys."""
-    n, levels = 1 << 24, 16
-    g = torch.Generator(device=dev)
-    g.manual_seed(6)
-    x = torch.randn(n, generator=g, device=dev, dtype=torch.float32)
+    n, levels = W.LLOYD["samples"], W.LLOYD["levels"]
+    xh = W.lloyd_samples()
+    x = torch.from_numpy(xh).to(dev)
     init = tq.lloyd_max_table(4)[0].astype("float64")
     ws = torch.empty(int(tq.lib().tq_lloyd_max_workspace_bytes(n)), dtype=torch.uint8, device=dev)
     log(f"workload lloyd_fit: {n} samples, {levels} levels, {iterations} iterations per step")
@@ -547,7 +548,7 @@ def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
         import numpy as np
         from oracle import lloyd as OL
         ns, it = 1 << 22, 25
-        xs = x[:ns].cpu().numpy()
+        xs = xh[:ns]
         t0 = time.perf_counter()
         OL.fit_samples(xs, init, it)
         t = time.perf_counter() - t0
@@ -622,6 +623,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph replay of the timed steps reported alongside")
+    ap.add_argument("--no-eager", action="store_true",
+                    help="deferred_v: skip timing the eager decode alongside (keeps a kernel trace to the timed steps)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -739,7 +742,7 @@ def main():
 
     dom = max(stats, key=lambda n: stats[n]["avg_us"])
     extra_fields = {}
-    if extra is not None:
+    if extra is not None and not args.no_eager:
         eager = extra()
         extra_fields["eager_decode"] = {"avg_us": eager, "rotated_decode_plus_unrotate_us":
                                         stats["decode"]["avg_us"] + stats["unrotate"]["avg_us"]}
@@ -752,8 +755,8 @@ def main():
     trace_fields = None if tr is None else {
         "source": f"profiles/{args.workload}_kernel_trace.json", "avg_us": tr["avg_us"],
         "frac": stats[dom]["bytes"] / (tr["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-        "p10_frac": stats[dom]["bytes"] / (tr["p90_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-        "p90_frac": stats[dom]["bytes"] / (tr["p10_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+        "p10_frac": None if tr["p90_us"] is None else stats[dom]["bytes"] / (tr["p90_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+        "p90_frac": None if tr["p10_us"] is None else stats[dom]["bytes"] / (tr["p10_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}
 
     out = {
         "metric": METRIC[args.workload],

@@ -8,7 +8,9 @@
 and 90th percentile / min durations from a ``--kernel-trace`` CSV, and with ``--stats`` the codec
 kernels' rows of rocprofv3's own ``--stats`` table; ``--json`` also writes the per-kind figures
 with the SHA-256 of each kind's sources (bench.py reports them beside its own timing when the
-sources still match). ``traffic`` turns the FETCH_SIZE and
+sources still match). ``counters`` summarises one ``--pmc`` pass of the SQ counters
+(instructions, busy cycles, wave cycles) per kernel kind with the derived
+clock, VALU busy fraction and occupancy. ``traffic`` turns the FETCH_SIZE and
 WRITE_SIZE counters (KiB per dispatch) of two ``--pmc`` runs of
 ``bench.py --copy-calibration-mib N`` into HBM bytes per launch: each
 counter is scaled by the factor that maps the same counter, read on the
@@ -167,6 +169,50 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, ops: dict | None = No
     return res
 
 
+SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
+               "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+
+# MI355X: 256 compute units of 4 SIMDs in 32 shader engines; SQ cycle
+# counters are summed over the shader engines, instruction counters over all
+# wavefronts, and SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES count 4-cycle units.
+N_SIMD, N_SE = 1024, 32
+
+
+def counter_summary(path: str) -> dict:
+    """Per kernel, the median per dispatch of each SQ counter in a
+    --pmc CSV, and derived figures: shader clock = SQ_BUSY_CYCLES / 32 /
+    duration; VALU busy = 4 * SQ_ACTIVE_INST_VALU / (1024 SIMDs * busy
+    cycles per engine); mean wavefronts per SIMD = 4 * SQ_WAVE_CYCLES /
+    (1024 * busy cycles per engine); VALU instructions per wavefront."""
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            kind = kernel_kind(r["Kernel_Name"])
+            if kind not in KINDS:
+                continue
+            key = (short_name(r["Kernel_Name"]), r["Dispatch_Id"])
+            d = per.setdefault(key, {"dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), "kind": kind})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    from kv_cache_quantization_tq_amd.build import source_digest
+    out = {}
+    for name in sorted({k for k, _ in per}):
+        ds = [d for (k, _), d in per.items() if k == name]
+        kind = ds[0]["kind"]
+        med = {c: statistics.median([d[c] for d in ds if c in d]) for c in ds[0] if c != "kind"}
+        res = {"kind": kind, "dispatches": len(ds), "source_sha256": source_digest(kind), "median": med}
+        if {"SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_WAVES"} <= set(med):
+            cyc = med["SQ_BUSY_CYCLES"] / N_SE
+            res["derived"] = {
+                "duration_us": med["dur_ns"] * 1e-3,
+                "shader_clock_GHz": cyc / med["dur_ns"],
+                "valu_busy": 4 * med["SQ_ACTIVE_INST_VALU"] / (N_SIMD * cyc),
+                "mean_waves_per_simd": 4 * med["SQ_WAVE_CYCLES"] / (N_SIMD * cyc),
+                "valu_insts_per_wave": med["SQ_INSTS_VALU"] / med["SQ_WAVES"],
+            }
+        out[name] = res
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -175,6 +221,9 @@ def main(argv=None):
     t.add_argument("--stats")
     t.add_argument("--ops", action="append", default=[], help="KIND=N: also report kernel time per operation")
     t.add_argument("--json", help="also write per-kind figures (with source digests) to this file")
+    q = sub.add_parser("counters")
+    q.add_argument("csv")
+    q.add_argument("--json")
     c = sub.add_parser("traffic")
     c.add_argument("fetch_csv")
     c.add_argument("write_csv")
@@ -192,6 +241,13 @@ def main(argv=None):
         if a.stats:
             print()
             print(stats_summary(a.stats))
+    elif a.cmd == "counters":
+        res = counter_summary(a.csv)
+        txt = json.dumps(res, indent=1)
+        if a.json:
+            with open(a.json, "w") as f:
+                f.write(txt + "\n")
+        print(txt)
     else:
         ops = {k: int(v) for k, v in (o.split("=") for o in a.ops)}
         res = traffic(a.fetch_csv, a.write_csv, a.copy_mib, ops)

@@ -178,6 +178,18 @@ def to_oracle(t) -> np.ndarray:
     return t.numpy()
 
 
+# ---------------------------------------------------------------- fitting
+
+LLOYD = dict(samples=1 << 24, levels=16, iterations=500, seed=6)
+
+
+def lloyd_samples(n: int = LLOYD["samples"], seed: int = LLOYD["seed"]) -> np.ndarray:
+    """The Lloyd-Max fit workload's samples: n unit-normal float32 draws from
+    numpy's PCG64 with `seed` (the tables page fits its tables to unit-normal
+    samples), drawn on the host so that any consumer can reproduce them."""
+    return np.random.default_rng(seed).standard_normal(n, dtype=np.float32)
+
+
 # ---------------------------------------------------------------- batching
 
 MERGE = dict(sequences=32, heads=8, head_dim=128, k_bits=4, v_bits=4, min_len=4096, max_len=32768, seed=5)

@@ -99,12 +99,15 @@ __device__ __forceinline__ float rows_sum(float x) { return swap_combine<false>(
 //           one quarter of its token's key row); it receives S[tokens 4 g ..
 //           4 g + 3][head h].
 //   output  O[16 dims x 16 heads] += V^T[dims x 16 tokens] * P^T[tokens x heads]
-//           (v_mfma_f32_16x16x16_bf16, one per 16 dims and weight term): lane
-//           l supplies V[tokens 4 g .. 4 g + 3][dim h] (a transposing LDS read
-//           of the wavefront's value tile) and the weights of those same
-//           tokens for head h -- exactly the scores it received, so the
-//           softmax needs no data movement; it accumulates O[dims 4 g .. 4 g +
-//           3][head h].
+//           (v_mfma_f32_16x16x16_bf16, one per output slice and weight term;
+//           slice n, n < W = D / 16, holds the 16 dims W m + n, m = 0 .. 15):
+//           lane l supplies V[tokens 4 g .. 4 g + 3][dim W h + n] and the
+//           weights of those same tokens for head h -- exactly the scores it
+//           received, so the softmax needs no data movement; it accumulates
+//           O[dims W (4 g + i) + n, i = 0 .. 3][head h]. Over all slices a
+//           lane's value operands are the W consecutive dims [W h, W h + W)
+//           of its four tokens, which it decodes itself from the packed rows
+//           (no transposition through LDS).
 //
 // Query heads beyond the KV head's group read an all-zero row and their
 // results are never used. Keys and values are bf16 (the decoders' output
@@ -125,16 +128,6 @@ constexpr int kTile = 16;                 // tokens per wavefront tile
 constexpr int kQRows = kAttnMaxG + 1;     // query rows in LDS; the last is zeros
 constexpr int kMaxQTerms = 3;
 
-// LDS layout of one wavefront's value tile (bf16): 16 token rows of D
-// elements, 2 D + 32 bytes apart (32 modulo 128), so that the 8-byte
-// transposing reads of a 16-lane group (four rows, 32 bytes each) fall on
-// distinct banks; the 16-byte row writes of the decoding lanes then meet at
-// most two to a bank.
-template <int D> struct VTile {
-    static constexpr int QE = D / 4;       // elements per quarter
-    static constexpr int RE = D + 16;      // elements per padded row
-    static constexpr int SPQ = D / 64;     // 16-element slices per quarter (D >= 64)
-};
 template <int D> constexpr int kQueryRow = D + 8; // elements per query row in LDS
 
 // One lane's quarter of a packed row: elements [s D/4, (s+1) D/4), held as
@@ -164,18 +157,36 @@ template <int NSW> __device__ __forceinline__ void load_scales(const uint8_t *p,
 
 // codes from the tile's first row `codes` (uniform) at lane byte offset
 // `off` (the lane's token row plus, at D >= 128, its quarter); scales from
-// `scale` (+ `zero`) at lane byte offset `soff`
+// `scale` (+ `zero`) at lane byte offset `soff`. Loads only: at D = 64 the
+// half group still has to be moved into place by finish_quarter, so that a
+// prefetched tile's loads stay in flight until the tile is used.
 template <int D, int B, bool ZERO>
 __device__ __forceinline__ void load_quarter(const uint8_t *codes, const uint8_t *scale, const uint8_t *zero,
-                                             uint32_t off, uint32_t soff, int s, Quarter<D, B> &q)
+                                             uint32_t off, uint32_t soff, Quarter<D, B> &q)
 {
     using Q = Quarter<D, B>;
     if constexpr (Q::E >= kGroup) {
 #pragma unroll
-        for (int gi = 0; gi < Q::NG; ++gi) load_codes<B>(codes + off + gi * (4 * B), q.w[gi]);
+        for (int gi = 0; gi < Q::NG; ++gi) {
+            const uint32_t o = off + gi * (4 * B);
+            load_codes<B>(codes + o, q.w[gi]);
+        }
     } else {
+        load_codes<B>(codes + off, q.w[0]);
+    }
+    load_scales<Q::NSW>(scale + soff, q.sc, Q::NG == 2);
+    if constexpr (ZERO) load_scales<Q::NSW>(zero + soff, q.zr, Q::NG == 2);
+}
+
+// at D = 64 a lane with odd s holds the upper half of its group: shift it
+// down so that its first code is code 0
+template <int D, int B> __device__ __forceinline__ void finish_quarter(Quarter<D, B> &q, int s)
+{
+    using Q = Quarter<D, B>;
+    if constexpr (Q::E < kGroup) {
         uint32_t t[B];
-        load_codes<B>(codes + off, t);
+#pragma unroll
+        for (int i = 0; i < B; ++i) t[i] = q.w[0][i];
         constexpr int sh_bits = kGroup / 2 * B, wo = sh_bits / 32, bs = sh_bits % 32;
         const bool upper = (s & 1) != 0;
 #pragma unroll
@@ -186,8 +197,6 @@ __device__ __forceinline__ void load_quarter(const uint8_t *codes, const uint8_t
             q.w[0][i] = upper ? sh : t[i];
         }
     }
-    load_scales<Q::NSW>(scale + soff, q.sc, Q::NG == 2);
-    if constexpr (ZERO) load_scales<Q::NSW>(zero + soff, q.zr, Q::NG == 2);
 }
 
 // the 8 codes first .. first + 7 (first a multiple of 8) of a group's words
@@ -216,132 +225,319 @@ template <int B> __device__ __forceinline__ void codes8(const uint32_t (&w)[B], 
     }
 }
 
+// 4-bit key codes are converted two at a time by reading them as FP8 (E4M3)
+// bytes: a byte 0 .. 15 has exponent field 0 or 1 and so encodes the integer
+// times the format's smallest subnormal, a power of two (2^-9 in the OCP
+// encoding). kKeyUnit(KB) is the factor a code's float carries: that power
+// of two for 4-bit unsigned codes, 1 otherwise (plain integer conversion).
+template <int KB, bool KS> constexpr bool kFp8Codes = KB == 4 && !KS;
+__device__ __forceinline__ float fp8_code_unit()
+{
+    return __builtin_amdgcn_cvt_pk_f32_fp8(0x0101, false)[0];
+}
+
+// elements 8 c .. 8 c + 7 of the quarter's key codes as floats, each the
+// code times the unit above (exact: the codes have at most 8 bits)
+template <int D, int KB, bool KS>
+__device__ __forceinline__ void key_code_floats(const Quarter<D, KB> &k, int c, float (&f)[8])
+{
+    const int gi = Quarter<D, KB>::NG > 1 ? 8 * c / kGroup : 0;
+    if constexpr (kFp8Codes<KB, KS>) {
+        // nibbles 0 .. 7 of the word are codes 8 c .. 8 c + 7; masks put the
+        // even codes in the bytes of lo and the odd ones in those of hi
+        const uint32_t x = k.w[gi][(8 * c) % kGroup / 8];
+        const uint32_t lo = x & 0x0f0f0f0fu, hi = (x >> 4) & 0x0f0f0f0fu;
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+        const auto e = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), o = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+        f[0] = a[0], f[2] = a[1], f[4] = b[0], f[6] = b[1];
+        f[1] = e[0], f[3] = e[1], f[5] = o[0], f[7] = o[1];
+    } else {
+        uint32_t q[8];
+        codes8<KB>(k.w[gi], (8 * c) % kGroup, q);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) f[u] = KS ? (float)(int32_t)(int8_t)(uint8_t)q[u] : (float)q[u];
+    }
+}
+
 // decodeKeys ((q + zero) * scale, rounded to bf16) of elements 8 c .. 8 c + 7
-// of the quarter, as packed bf16 pairs. FMA: as fma(q, scale, zero * scale)
-// (zs = zero * scale), used when every group of the wavefront's tile has a
+// of the quarter, as packed bf16 pairs, from the codes as floats f (code
+// times unit). FMA: as fma(f, scale / unit, zero * scale) (su = scale / unit,
+// zs = zero * scale), used when every group of the wavefront's tile has a
 // finite nonzero scale and a finite zero point: a code has at most 8
 // significant bits and an fp16 scale or zero at most 11, so both products
-// are exact in binary32, q + zero is an exact integer, and the fma's single
-// rounding is that of (q + zero) * scale. Otherwise the two-step form (which
-// also fixes the sign of a zero result).
-template <int D, int KB, bool KS, bool FMA>
-__device__ __forceinline__ u32x4_t key_chunk(const Quarter<D, KB> &k, int c, const float (&sc)[Quarter<D, KB>::NG],
-                                             const float (&zr)[Quarter<D, KB>::NG],
+// are exact in binary32 (unit being a power of two), q + zero is an exact
+// integer, and the fma's single rounding is that of (q + zero) * scale.
+// Otherwise the two-step form on q = f / unit (which also fixes the sign of
+// a zero result).
+template <int D, int KB, bool FMA>
+__device__ __forceinline__ u32x4_t key_chunk(const float (&f)[8], int c, float inv_unit, const Quarter<D, KB> &k,
+                                             const float (&su)[Quarter<D, KB>::NG],
                                              const float (&zs)[Quarter<D, KB>::NG])
 {
     const int gi = Quarter<D, KB>::NG > 1 ? 8 * c / kGroup : 0;
-    uint32_t q[8];
-    codes8<KB>(k.w[gi], (8 * c) % kGroup, q);
+    const float sc = FMA ? 0.0f : f16_bits_to_f32(k.scale(gi)), zr = FMA ? 0.0f : f16_bits_to_f32(k.zero(gi));
     u32x4_t r;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        float f[2];
+        float y[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const uint32_t x = q[2 * w + u];
-            const float qf = KS ? (float)(int32_t)(int8_t)(uint8_t)x : (float)x;
-            f[u] = FMA ? __builtin_fmaf(qf, sc[gi], zs[gi]) : (qf + zr[gi]) * sc[gi];
+            const float x = f[2 * w + u];
+            y[u] = FMA ? __builtin_fmaf(x, su[gi], zs[gi]) : (x * inv_unit + zr) * sc;
         }
-        r[w] = pack_bf16x2(f[0], f[1]);
+        r[w] = pack_bf16x2(y[0], y[1]);
     }
     return r;
 }
 
-// decodeValuesRotated (centroid * scale, rounded to bf16) of elements 8 c ..
-// 8 c + 7 of the quarter, as packed bf16 pairs
+// One lane's values of a tile: tokens 4 g + i (i = 0 .. 3), dims [W h, W h
+// + W), W = D / 16 (inside one group, W dividing 32): per token the window's
+// code bits shifted to start at bit 0, and the group's fp16 scale.
+template <int D, int VB> struct VWin {
+    static constexpr int W = D / 16;          // dims of a window
+    static constexpr int WB = W * VB;         // its code bits
+    static constexpr int NW = (WB + 31) / 32; // words of a window from bit 0
+    // words covering lane h's window, which starts at bit WB h of the row
+    static constexpr int need(int h) { return ((WB * h) % 32 + WB + 31) / 32; }
+    static constexpr int most_words()
+    {
+        int m = 0;
+        for (int h = 0; h < 16; ++h) m = need(h) > m ? need(h) : m;
+        return m;
+    }
+    static constexpr bool same_for_all()
+    {
+        for (int h = 0; h < 16; ++h)
+            if (need(h) != most_words()) return false;
+        return true;
+    }
+    static constexpr int RW = most_words(); // words loaded per token, at most
+    static constexpr bool ALL = same_for_all(); // every lane loads RW words
+    uint32_t w[4][NW];
+    uint32_t sc[2]; // fp16 scales, token 2 k + u in bits 16 u of word k
+    __device__ __forceinline__ float scale(int i) const { return f16_bits_to_f32((uint16_t)(sc[i / 2] >> (16 * (i & 1)))); }
+};
+
+// the words covering the windows of the lane's four tokens, from the tile's
+// first code row `codes`, and their group scales from the first scale row
+// `scales`; voff[i] and soff[i]: the byte offsets of token i's first word
+// and of its scale. A lane loads only the words its window covers, so that
+// no read passes the end of the last row. Loads only (see finish_vwin).
+template <int D, int VB> struct VRaw {
+    uint32_t r[4][VWin<D, VB>::RW];
+    uint32_t s[4];
+};
 template <int D, int VB>
-__device__ __forceinline__ u32x4_t value_chunk(const Quarter<D, VB> &v, int c, const float *cent,
-                                               const float (&sc)[Quarter<D, VB>::NG])
+__device__ __forceinline__ void load_vwin(const uint8_t *codes, const uint8_t *scales, const uint32_t (&voff)[4],
+                                          const uint32_t (&soff)[4], int h, VRaw<D, VB> &v)
 {
-    const int gi = Quarter<D, VB>::NG > 1 ? 8 * c / kGroup : 0;
-    uint32_t q[8];
-    codes8<VB>(v.w[gi], (8 * c) % kGroup, q);
-    u32x4_t r;
+    using V = VWin<D, VB>;
+    const uint32_t sh = (uint32_t)(V::WB * h) % 32;
+    const uint32_t nw = (sh + V::WB + 31) / 32;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) r[k] = pack_bf16x2(cent[q[2 * k]] * sc[gi], cent[q[2 * k + 1]] * sc[gi]);
-    return r;
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(codes + voff[i]);
+#pragma unroll
+        for (int k = 0; k < V::RW; ++k) v.r[i][k] = (V::ALL || k == 0 || (uint32_t)k < nw) ? src[k] : 0u;
+        v.s[i] = *reinterpret_cast<const uint16_t *>(scales + soff[i]);
+    }
+}
+
+// the windows shifted to start at bit 0, and the scales two to a word
+template <int D, int VB> __device__ __forceinline__ void finish_vwin(const VRaw<D, VB> &raw, int h, VWin<D, VB> &v)
+{
+    using V = VWin<D, VB>;
+    const uint32_t sh = (uint32_t)(V::WB * h) % 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int k = 0; k < V::NW; ++k)
+            v.w[i][k] = __builtin_amdgcn_alignbit(k + 1 < V::RW ? raw.r[i][k + 1] : 0u, raw.r[i][k], sh);
+    }
+    v.sc[0] = raw.s[0] | (raw.s[1] << 16);
+    v.sc[1] = raw.s[2] | (raw.s[3] << 16);
+}
+
+// byte offsets within a tile of the lane's value windows and scales for
+// tokens t0 + i, i = 0 .. 3, clamped to the tile's last valid token nv - 1
+template <int D, int VB>
+__device__ __forceinline__ void vwin_offsets(int t0, int h, int nv, uint32_t vstride, uint32_t sstride,
+                                             uint32_t (&voff)[4], uint32_t (&soff)[4])
+{
+    using V = VWin<D, VB>;
+    const uint32_t wo = (uint32_t)(V::WB * h) / 32 * 4, so = (uint32_t)(V::W * h / kGroup) * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = (uint32_t)(t0 + i < nv ? t0 + i : nv - 1);
+        voff[i] = t * vstride + wo;
+        soff[i] = t * sstride + so;
+    }
+}
+
+// Value lookup table in LDS. With pairs (VB < 8), entry (c1 << VB) | c0
+// holds the centroids of c0 and c1 (8 bytes), so that two consecutive codes
+// -- one 2 VB-bit field of a window -- are looked up at once; otherwise the
+// centroids themselves (4 bytes each).
+template <int VB> constexpr bool kPairTable = VB < 8;
+template <int VB> constexpr int kVTabBytes = kPairTable<VB> ? (8 << (2 * VB)) : (4 << VB);
+
+// byte offset in the table of field i of a window: pair i (codes 2 i,
+// 2 i + 1) with pairs, else code i
+template <int VB, int NW> __device__ __forceinline__ uint32_t vtab_offset(const uint32_t (&w)[NW], int i)
+{
+    constexpr int FB = kPairTable<VB> ? 2 * VB : VB; // bits of a field
+    constexpr int LS = kPairTable<VB> ? 3 : 2;       // log2 of an entry's bytes
+    constexpr uint32_t M = ((1u << FB) - 1) << LS;
+    const int p = FB * i - LS;                       // where the scaled field starts
+    if (p < 0) return (w[0] << LS) & M;
+    const int k = p / 32, s = p % 32;
+    const uint32_t x = (s + FB + LS <= 32) ? (w[k] >> s) : __builtin_amdgcn_alignbit(w[k + 1], w[k], s);
+    return x & M;
+}
+
+// the centroids of the lane's operands of output slices 2 i and 2 i + 1:
+// c0[t], c1[t] for dims W h + 2 i and W h + 2 i + 1 of token 4 g + t
+struct VLook {
+    float c0[4], c1[4];
+};
+template <int D, int VB>
+__device__ __forceinline__ void value_lookup(const VWin<D, VB> &v, int i, const uint8_t *tab, VLook &l)
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        if constexpr (kPairTable<VB>) {
+            const float2 c = *reinterpret_cast<const float2 *>(tab + vtab_offset<VB>(v.w[t], i));
+            l.c0[t] = c.x;
+            l.c1[t] = c.y;
+        } else {
+            l.c0[t] = *reinterpret_cast<const float *>(tab + vtab_offset<VB>(v.w[t], 2 * i));
+            l.c1[t] = *reinterpret_cast<const float *>(tab + vtab_offset<VB>(v.w[t], 2 * i + 1));
+        }
+    }
+}
+
+// decodeValuesRotated (centroid * scale, rounded to bf16) of those
+// operands: V[token 4 g + t][dim W h + n], t = 0 .. 3, for n = 2 i (a0) and
+// n = 2 i + 1 (a1)
+__device__ __forceinline__ void value_operands(const VLook &l, const float (&sc)[4], s16x4_t &a0, s16x4_t &a1)
+{
+    float x[4], y[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        x[t] = l.c0[t] * sc[t];
+        y[t] = l.c1[t] * sc[t];
+    }
+    a0 = __builtin_bit_cast(s16x4_t, u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
+    a1 = __builtin_bit_cast(s16x4_t, u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])});
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xffff0000u); }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMax = 8.0f; // see the softmax in wave_tiles
 
 // The tiles of one wavefront: tokens [t_lo, t_end) of (sequence b, KV
 // head j), 16 at a time, with an online softmax per query head in base 2
 // (scores scaled by scale * log2(e) and exponentiated with exp2, so the
 // running maximum is a base-2 logarithm). QT is the number of bf16 terms of
-// the query. Per tile: the 32-element chunks of keys (straight into the
-// matrix cores) and of values (into the wavefront's LDS tile) are decoded
-// in one loop, so that either's LDS waits overlap the other's arithmetic;
-// then the softmax and the weighted values.
+// the query. Per tile: the packed keys and values are loaded at the top;
+// the keys' 32-element chunks are decoded straight into the matrix cores;
+// then the softmax, and the values are decoded, slice pair by slice pair,
+// into the operands of the weighted sum. tab: the value lookup table.
 template <int D, int VB, int KB, bool KS, int QT>
 __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, int64_t t_lo, int64_t t_end,
-                                           const float *cent, uint16_t *vt, const uint16_t *qrow,
-                                           f32x4_t (&acc)[D / 16], float &m_run, float &l_run)
+                                           const uint8_t *tab, const uint16_t *qrow, f32x4_t (&acc)[D / 16],
+                                           float &m_run, float &l_run)
 {
-    using VT = VTile<D>;
     using KQ = Quarter<D, KB>;
-    using VQ = Quarter<D, VB>;
+    using VW = VWin<D, VB>;
     constexpr int G = D / kGroup;
     constexpr int NC = D / 32;  // 32-element chunks of the contraction (and 8-element chunks of a quarter)
-    constexpr int NS = D / 16;  // 16-dim output slices
+    constexpr int NS = D / 16;  // output slices
     constexpr int QR = kQueryRow<D>;
     constexpr uint32_t KROW = D * KB / 8, VROW = D * VB / 8; // code bytes per row
     const int lane = threadIdx.x & (kWave - 1);
     const int h = lane & 15, g = lane >> 4;
-    const uint16_t *vread = vt + (4 * g + (h >> 2)) * VT::RE + 4 * (h & 3);
-    uint16_t *vwrite = vt + h * VT::RE + g * VT::QE;
     // per-token strides of the planes (a token's rows of all KV heads are
     // adjacent) and the lanes' offsets within a token row
     const uint32_t kstride = (uint32_t)p.hkv * KROW, vstride = (uint32_t)p.hkv * VROW;
     const uint32_t sstride = (uint32_t)p.hkv * G * 2;
     const uint32_t kq_off = KQ::E >= kGroup ? g * (KROW / 4) : (g >> 1) * (4 * KB);
-    const uint32_t vq_off = VQ::E >= kGroup ? g * (VROW / 4) : (g >> 1) * (4 * VB);
     const uint32_t ks_off = KQ::E >= kGroup ? g * KQ::NG * 2 : (g >> 1) * 2;
-    const uint32_t vs_off = VQ::E >= kGroup ? g * VQ::NG * 2 : (g >> 1) * 2;
     const float sl2 = p.scale * kLog2e;
+    // 1 / (the factor a key code's float carries), an exact power of two
+    const float inv_unit = kFp8Codes<KB, KS> ? 1.0f / fp8_code_unit() : 1.0f;
 
-    for (int64_t t0 = t_lo; t0 < t_end; t0 += kTile) {
-        // the tile's first row (uniform) and each lane's token, clamped to
-        // the tile's last valid token
+    // the lanes' byte offsets within a full tile (key token h, value tokens
+    // 4 g + i: the first, plus i token strides); a partial tile clamps them
+    // to its last valid token
+    const uint32_t koff_full = h * kstride + kq_off, ksoff_full = h * sstride + ks_off;
+    uint32_t voff0, vsoff0;
+    {
+        uint32_t vo[4], so[4];
+        vwin_offsets<D, VB>(4 * g, h, kTile, vstride, sstride, vo, so);
+        voff0 = vo[0];
+        vsoff0 = so[0];
+    }
+
+    // the packed rows of the tile at t0
+    auto load_tile = [&](int64_t t0, KQ &kq, VRaw<D, VB> &vr) {
         const int64_t row0 = ((int64_t)b * p.width + t0) * p.hkv + j;
         const int nv = (int)(t_end - t0 < kTile ? t_end - t0 : kTile);
-        const uint32_t tk = (uint32_t)(h < nv ? h : nv - 1);
-        KQ kq;
-        VQ vq;
+        uint32_t koff = koff_full, ksoff = ksoff_full, voff[4], vsoff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) voff[i] = voff0 + i * vstride, vsoff[i] = vsoff0 + i * sstride;
+        if (nv < kTile) { // wavefront-uniform: the wavefront's last tile
+            const uint32_t tk = (uint32_t)(h < nv ? h : nv - 1);
+            koff = tk * kstride + kq_off;
+            ksoff = tk * sstride + ks_off;
+            vwin_offsets<D, VB>(4 * g, h, nv, vstride, sstride, voff, vsoff);
+        }
         load_quarter<D, KB, true>(p.kc + row0 * KROW, reinterpret_cast<const uint8_t *>(p.ks + row0 * G),
-                                  reinterpret_cast<const uint8_t *>(p.kz + row0 * G), tk * kstride + kq_off,
-                                  tk * sstride + ks_off, g, kq);
-        load_quarter<D, VB, false>(p.vc + row0 * VROW, reinterpret_cast<const uint8_t *>(p.vs + row0 * G), nullptr,
-                                   tk * vstride + vq_off, tk * sstride + vs_off, g, vq);
+                                  reinterpret_cast<const uint8_t *>(p.kz + row0 * G), koff, ksoff, kq);
+        load_vwin<D, VB>(p.vc + row0 * VROW, reinterpret_cast<const uint8_t *>(p.vs + row0 * G), voff, vsoff, h, vr);
+    };
 
-        // scores of the tile's 16 tokens; values into the LDS tile
-        float ksc[KQ::NG], kzr[KQ::NG], kzs[KQ::NG], vsc[VQ::NG];
+    // one tile, from its loaded rows
+    auto tile = [&](int64_t t0, KQ &kq, const VRaw<D, VB> &vr) {
+        const int nv = (int)(t_end - t0 < kTile ? t_end - t0 : kTile);
+        finish_quarter<D, KB>(kq, g);
+        VW vw;
+        finish_vwin<D, VB>(vr, h, vw);
+
+        // scores of the tile's 16 tokens
+        float ksu[KQ::NG], kzs[KQ::NG];
         bool fma_ok = true;
 #pragma unroll
         for (int gi = 0; gi < KQ::NG; ++gi) {
-            ksc[gi] = f16_bits_to_f32(kq.scale(gi));
-            kzr[gi] = f16_bits_to_f32(kq.zero(gi));
-            kzs[gi] = kzr[gi] * ksc[gi];
-            fma_ok = fma_ok && ksc[gi] != 0.0f && __builtin_isfinite(kzs[gi]);
+            const float ksc = f16_bits_to_f32(kq.scale(gi));
+            ksu[gi] = ksc * inv_unit;
+            kzs[gi] = f16_bits_to_f32(kq.zero(gi)) * ksc;
+            fma_ok = fma_ok && ksc != 0.0f && __builtin_isfinite(kzs[gi]);
         }
         const bool tile_fma = __all(fma_ok);
-#pragma unroll
-        for (int gi = 0; gi < VQ::NG; ++gi) vsc[gi] = f16_bits_to_f32(vq.scale(gi));
         f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-            u32x4_t kc = key_chunk<D, KB, KS, true>(kq, cc, ksc, kzr, kzs);
-            if (!tile_fma) kc = key_chunk<D, KB, KS, false>(kq, cc, ksc, kzr, kzs); // wavefront-uniform, rare
+            float kf[8];
+            key_code_floats<D, KB, KS>(kq, cc, kf);
+            u32x4_t kc;
+            if (tile_fma) // wavefront-uniform; the other form is rare
+                kc = key_chunk<D, KB, true>(kf, cc, inv_unit, kq, ksu, kzs);
+            else
+                kc = key_chunk<D, KB, false>(kf, cc, inv_unit, kq, ksu, kzs);
             const bf16x8_t a = __builtin_bit_cast(bf16x8_t, kc);
 #pragma unroll
             for (int t = 0; t < QT; ++t) {
                 const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(qrow + t * (kQRows * QR) + 8 * cc);
                 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, qv), S, 0, 0, 0);
             }
-            *reinterpret_cast<u32x4_t *>(vwrite + 8 * cc) = value_chunk<D, VB>(vq, cc, cent, vsc);
         }
+
+        // the first slice pair's value lookups, in flight during the softmax
+        VLook look;
+        value_lookup<D, VB>(vw, 0, tab, look);
 
         // online softmax: lane (h, g) holds tokens 4 g .. 4 g + 3 for head h
         float s4[4];
@@ -352,14 +548,19 @@ __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, in
             mx = fmaxf(mx, s4[i]);
         }
         mx = rows_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const bool live = m_new != -INFINITY;
-        const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        // the reference maximum m_run moves only when the tile's maximum
+        // passes it by more than kLazyMax (base 2), so that the accumulators
+        // are rescaled rarely; meanwhile the weights exp2(s - m_run) stay
+        // below 2^kLazyMax (their three-term split is as exact at any size)
+        const bool grow = !(mx <= m_run + kLazyMax);
+        const float m_ref = grow ? fmaxf(m_run, mx) : m_run;
+        const bool live = m_ref != -INFINITY;
+        const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.0f;
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = live ? __builtin_amdgcn_exp2f(s4[i] - m_new) : 0.0f;
+        for (int i = 0; i < 4; ++i) pr[i] = live ? __builtin_amdgcn_exp2f(s4[i] - m_ref) : 0.0f;
         l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        m_run = m_new;
+        m_run = m_ref;
         s16x4_t pt[kMaxQTerms];
 #pragma unroll
         for (int t = 0; t < kMaxQTerms; ++t) {
@@ -374,20 +575,47 @@ __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, in
 #pragma unroll
             for (int n = 0; n < NS; ++n) acc[n] *= alpha;
         }
-        wave_lds_sync();
 
         // weighted values
+        float vsc[4];
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-            const uint16_t *src = vread + (n / VT::SPQ) * VT::QE + (n % VT::SPQ) * 16;
-            const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t *)(src));
+        for (int i = 0; i < 4; ++i) vsc[i] = vw.scale(i);
 #pragma unroll
-            for (int t = 0; t < kMaxQTerms; ++t)
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pt[t], acc[n], 0, 0, 0);
+        for (int i = 0; i < NS / 2; ++i) {
+            // the next pair's lookups go out before this pair's arithmetic
+            VLook next;
+            if (i + 1 < NS / 2) value_lookup<D, VB>(vw, i + 1, tab, next);
+            s16x4_t a0, a1;
+            value_operands(look, vsc, a0, a1);
+#pragma unroll
+            for (int t = 0; t < kMaxQTerms; ++t) {
+                acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, pt[t], acc[2 * i], 0, 0, 0);
+                acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, pt[t], acc[2 * i + 1], 0, 0, 0);
+            }
+            look = next;
+            // one pair ahead at most: the scheduler would otherwise hoist
+            // every pair's lookups to the top (registers for all at once)
+            __builtin_amdgcn_sched_barrier(0);
         }
-        wave_lds_sync();
+    };
+
+    for (int64_t t0 = t_lo; t0 < t_end; t0 += kTile) {
+        KQ kq;
+        VRaw<D, VB> vr;
+        load_tile(t0, kq, vr);
+        tile(t0, kq, vr);
     }
+}
+
+// Dynamic LDS of a partial block: the query terms [q_terms][kQRows][D + 8]
+// bf16; after the tiles the same bytes hold the merge area, two slots of
+// [g][D + 4] floats.
+template <int D> constexpr int kMergeRow = D + 4;
+int64_t partial_lds_bytes(int d, int q_terms, int g)
+{
+    const int64_t query = (int64_t)q_terms * kQRows * (d + 8) * 2;
+    const int64_t merge = (int64_t)2 * g * (d + 4) * 4;
+    return query > merge ? query : merge;
 }
 
 // Blocks are ordered so that the KV heads of one (sequence, chunk) are
@@ -400,14 +628,14 @@ __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, in
 template <int D, int VB, int KB, bool KS>
 __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams p)
 {
-    using VT = VTile<D>;
-    constexpr int NS = D / 16;  // 16-dim output slices
+    constexpr int NS = D / 16;  // output slices
+    constexpr int W = D / 16;   // slice n holds dims W m + n
     constexpr int QR = kQueryRow<D>;
-    __shared__ float cent[1 << VB];
-    __shared__ __align__(16) uint16_t vtile[kWavesPerBlock][kTile][VT::RE];
+    constexpr int SR = kMergeRow<D>;
+    __shared__ __align__(16) uint8_t tab[kVTabBytes<VB>];
     __shared__ float ml[kWavesPerBlock][kAttnMaxG][2];
-    extern __shared__ __align__(16) uint16_t qlds[]; // [q_terms][kQRows][QR] bf16
-    static_assert(sizeof(float) * kWavesPerBlock * kAttnMaxG * D <= sizeof(vtile), "merge area");
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint16_t *qlds = reinterpret_cast<uint16_t *>(lds);
 
     const int id = blockIdx.x;
     const int x = id % 8, r = id / 8;
@@ -417,7 +645,15 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     const int b = cg / p.nsplit, c = cg % p.nsplit;
     const int gq = p.g, hq = p.hkv * p.g;
     const int tid = threadIdx.x;
-    for (int i = tid; i < (1 << VB); i += kBlockThreads) cent[i] = dev_cent<VB>()[i];
+    const float *cent = dev_cent<VB>();
+    if constexpr (kPairTable<VB>) {
+        float2 *t2 = reinterpret_cast<float2 *>(tab);
+        for (int i = tid; i < (1 << (2 * VB)); i += kBlockThreads)
+            t2[i] = make_float2(cent[i & ((1 << VB) - 1)], cent[i >> VB]);
+    } else {
+        float *t1 = reinterpret_cast<float *>(tab);
+        for (int i = tid; i < (1 << VB); i += kBlockThreads) t1[i] = cent[i];
+    }
     for (int i = tid; i < kQRows * D; i += kBlockThreads) {
         const int e = i / D, k = i % D;
         float xq = 0.0f;
@@ -448,41 +684,68 @@ __global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams 
     for (int n = 0; n < NS; ++n) acc[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;
     if (p.q_terms == 1)
-        wave_tiles<D, VB, KB, KS, 1>(p, b, j, t_lo, t_end, cent, &vtile[wave][0][0], qrow, acc, m_run, l_run);
+        wave_tiles<D, VB, KB, KS, 1>(p, b, j, t_lo, t_end, tab, qrow, acc, m_run, l_run);
     else
-        wave_tiles<D, VB, KB, KS, kMaxQTerms>(p, b, j, t_lo, t_end, cent, &vtile[wave][0][0], qrow, acc, m_run,
-                                              l_run);
+        wave_tiles<D, VB, KB, KS, kMaxQTerms>(p, b, j, t_lo, t_end, tab, qrow, acc, m_run, l_run);
 
-    // merge the block's four wavefront splits through the (now free) value
-    // tiles, [wave][head][D] floats, and write the block's partial rows
+    // merge the block's four wavefront splits: each scales its sums to the
+    // block's maximum, then wavefronts 2 and 3 hand theirs to 0 and 1, and
+    // 1 to 0, through two slots of [head][dim] floats (dim W m + n at
+    // n * 16 + m) over the query terms, which the tiles no longer use
     l_run = rows_sum(l_run);
+    if (h < gq && g == 0) {
+        ml[wave][h][0] = m_run;
+        ml[wave][h][1] = l_run;
+    }
     __syncthreads();
-    float *scr = reinterpret_cast<float *>(&vtile[0][0][0]);
-    if (h < gq) {
+    const bool mine = h < gq;
+    if (mine) {
+        float M = ml[0][h][0];
 #pragma unroll
-        for (int n = 0; n < NS; ++n)
-            *reinterpret_cast<f32x4_t *>(&scr[(wave * gq + h) * D + n * 16 + 4 * g]) = acc[n];
-        if (g == 0) {
-            ml[wave][h][0] = m_run;
-            ml[wave][h][1] = l_run;
+        for (int v = 1; v < kWavesPerBlock; ++v) M = fmaxf(M, ml[v][h][0]);
+        const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+#pragma unroll
+        for (int n = 0; n < NS; ++n) acc[n] *= f;
+    }
+    float *slot0 = reinterpret_cast<float *>(lds), *slot1 = slot0 + gq * SR;
+    float *own = (wave & 1) ? slot1 : slot0; // the slot of wavefronts 1 and 3 / 0 and 2
+    if (wave >= 2 && mine) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) *reinterpret_cast<f32x4_t *>(&own[h * SR + n * 16 + 4 * g]) = acc[n];
+    }
+    __syncthreads();
+    if (wave < 2 && mine) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) acc[n] += *reinterpret_cast<const f32x4_t *>(&own[h * SR + n * 16 + 4 * g]);
+    }
+    __syncthreads();
+    if (wave == 1 && mine) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) *reinterpret_cast<f32x4_t *>(&slot0[h * SR + n * 16 + 4 * g]) = acc[n];
+    }
+    __syncthreads();
+    if (wave == 0 && mine) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            acc[n] += *reinterpret_cast<const f32x4_t *>(&slot0[h * SR + n * 16 + 4 * g]);
+            *reinterpret_cast<f32x4_t *>(&slot1[h * SR + n * 16 + 4 * g]) = acc[n];
         }
     }
     __syncthreads();
     for (int i = tid; i < gq * D; i += kBlockThreads) {
         const int e = i / D, k = i % D;
-        float M = ml[0][e][0];
-#pragma unroll
-        for (int v = 1; v < kWavesPerBlock; ++v) M = fmaxf(M, ml[v][e][0]);
-        float a = 0.0f, L = 0.0f;
-#pragma unroll
-        for (int v = 0; v < kWavesPerBlock; ++v) {
-            const float f = ml[v][e][0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[v][e][0] - M);
-            L = fmaf(ml[v][e][1], f, L);
-            a = fmaf(scr[(v * gq + e) * D + k], f, a);
-        }
         float *row = part_row<D>(p, b, j * gq + e, c);
-        row[k] = a;
+        row[k] = slot1[e * SR + (k % W) * 16 + k / W];
         if (k == 0) {
+            float M = ml[0][e][0];
+#pragma unroll
+            for (int v = 1; v < kWavesPerBlock; ++v) M = fmaxf(M, ml[v][e][0]);
+            float L = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kWavesPerBlock; ++v) {
+                const float f = ml[v][e][0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[v][e][0] - M);
+                L = fmaf(ml[v][e][1], f, L);
+            }
             row[D] = M;
             row[D + 1] = L;
         }
@@ -755,8 +1018,8 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
                        : d == 128 ? partial_kernel_for<128>(cfg->v_bits, kmode)
                        : d == 256 ? partial_kernel_for<256>(cfg->v_bits, kmode)
                                   : partial_kernel_for<512>(cfg->v_bits, kmode);
-        const size_t qlds_bytes = (size_t)p.q_terms * kQRows * (d + 8) * sizeof(uint16_t);
-        nch = n_splits(batch, kv_heads, width, resident_blocks(fn, qlds_bytes));
+        const size_t lds_bytes = (size_t)partial_lds_bytes(d, p.q_terms, p.g);
+        nch = n_splits(batch, kv_heads, width, resident_blocks(fn, lds_bytes));
         if (nch > kAttnMaxSplits || wave_tokens(width, nch) > 0x7fffffff) return TQ_E_SHAPE;
         p.nsplit = (int32_t)nch;
         p.wave_tokens = (int32_t)wave_tokens(width, nch);
@@ -764,7 +1027,7 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
         const int64_t blocks = groups * 8 * kv_heads;
         if (blocks > 0x7fffffff) return TQ_E_SHAPE;
         void *args[] = {&p};
-        if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kBlockThreads), args, qlds_bytes,
+        if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kBlockThreads), args, lds_bytes,
                             (hipStream_t)stream) != hipSuccess)
             return TQ_E_HIP;
     }

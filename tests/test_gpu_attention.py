@@ -40,12 +40,13 @@ def to_dev(planes, dev):
 
 
 def case(dev, *, d, kb, vb, ks=False, g=1, hkv=2, batch=1, width=700, pads=None, seed=0, q_bf16=False,
-         out_bf16=False, scale=None, kscale=1.0):
+         out_bf16=False, scale=None, kscale=1.0, zero_key_rows=()):
     print(f"[attention] d={d} k{kb}{'s' if ks else ''} v{vb} g={g} hkv={hkv} batch={batch} width={width} "
-          f"pads={pads} q_bf16={q_bf16} out_bf16={out_bf16}", flush=True)
+          f"pads={pads} q_bf16={q_bf16} out_bf16={out_bf16} zero_key_rows={len(zero_key_rows)}", flush=True)
     rng = np.random.default_rng(seed)
     rows = batch * width * hkv
     k = (rng.standard_normal((rows, d)) * kscale).astype(np.float32)
+    k[list(zero_key_rows)] = 0.0
     v = rng.standard_normal((rows, d)).astype(np.float32)
     planes = O.encode_kv(k, v, head_dim=d, k_bits=kb, v_bits=vb, k_signed=ks)
     q = rng.standard_normal((batch, hkv * g, d)).astype(np.float32)
@@ -83,6 +84,23 @@ def test_head_dims_and_groups(dev, d, g):
 @pytest.mark.parametrize("kb,vb,ks", [(2, 2, False), (3, 3, False), (5, 5, False), (8, 8, False), (8, 3, True)])
 def test_bit_widths(dev, kb, vb, ks):
     case(dev, d=128, kb=kb, vb=vb, ks=ks, g=4, seed=10 * kb + vb)
+
+
+@pytest.mark.parametrize("vb", [3, 5])
+def test_value_windows_off_byte_boundaries(dev, vb):
+    # at d = 64 a lane's window of 4 odd-width codes starts inside a byte and
+    # the lanes differ in how many words it spans
+    case(dev, d=64, kb=4, vb=vb, g=4, width=1000, seed=20 + vb)
+
+
+@pytest.mark.parametrize("kb,ks", [(4, False), (8, True)])
+def test_zero_key_groups_take_the_two_step_decode(dev, kb, ks):
+    # all-zero key rows give groups of scale 0, for which the fused
+    # multiply-add form of the key decode does not apply: a run of 16 tokens
+    # of one KV head and scattered single rows of the other
+    hkv, width = 2, 700
+    rows = [(t * hkv) for t in range(32, 48)] + [t * hkv + 1 for t in (5, 100, 333, 699)]
+    case(dev, d=256, kb=kb, vb=5, ks=ks, g=4, hkv=hkv, width=width, seed=30 + kb, zero_key_rows=rows)
 
 
 def test_left_padded_batch_with_an_empty_sequence(dev):

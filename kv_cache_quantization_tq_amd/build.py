@@ -132,5 +132,29 @@ def build_asm(out_dir: str) -> None:
         list(ex.map(_run, cmds))
 
 
+def kernel_resources(srcs=None) -> dict:
+    """Per kernel of the device code: VGPRs (next free), LDS and scratch
+    (private segment) bytes, read from the assembly hipcc produces with the
+    build's flags. Scratch means register spills, which the kernels are
+    written to avoid."""
+    import re
+    srcs = sources() if srcs is None else srcs
+    res = {}
+    with tempfile.TemporaryDirectory() as tmp:
+        outs = [os.path.join(tmp, os.path.basename(s) + ".s") for s in srcs]
+        cmds = [[hipcc(), *[f for f in _flags(s) if f != "-fPIC"], "--cuda-device-only", "-S", "-o", o, s]
+                for s, o in zip(srcs, outs)]
+        with cf.ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
+            list(ex.map(_run, cmds))
+        for o in outs:
+            text = open(o).read()
+            for m in re.finditer(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S):
+                body = m.group(2)
+                field = lambda k: int(re.search(k + r" (\d+)", body).group(1))
+                res[m.group(1)] = {"vgpr": field("next_free_vgpr"), "lds": field("group_segment_fixed_size"),
+                                   "scratch": field("private_segment_fixed_size")}
+    return res
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -441,10 +441,10 @@ constexpr float kLazyMax = 8.0f; // see the softmax in wave_tiles
 // head j), 16 at a time, with an online softmax per query head in base 2
 // (scores scaled by scale * log2(e) and exponentiated with exp2, so the
 // running maximum is a base-2 logarithm). QT is the number of bf16 terms of
-// the query. Per tile: the packed keys and values are loaded at the top;
-// the keys' 32-element chunks are decoded straight into the matrix cores;
-// then the softmax, and the values are decoded, slice pair by slice pair,
-// into the operands of the weighted sum. tab: the value lookup table.
+// the query. Per tile: the packed keys are loaded and their 32-element
+// chunks decoded straight into the matrix cores; then the value windows are
+// loaded, and after the softmax decoded, slice pair by slice pair, into the
+// operands of the weighted sum. tab: the value lookup table.
 template <int D, int VB, int KB, bool KS, int QT>
 __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, int64_t t_lo, int64_t t_end,
                                            const uint8_t *tab, const uint16_t *qrow, f32x4_t (&acc)[D / 16],
@@ -481,30 +481,24 @@ __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, in
         vsoff0 = so[0];
     }
 
-    // the packed rows of the tile at t0
-    auto load_tile = [&](int64_t t0, KQ &kq, VRaw<D, VB> &vr) {
+    // the packed key rows of the tile at t0
+    auto load_keys = [&](int64_t t0, KQ &kq) {
         const int64_t row0 = ((int64_t)b * p.width + t0) * p.hkv + j;
         const int nv = (int)(t_end - t0 < kTile ? t_end - t0 : kTile);
-        uint32_t koff = koff_full, ksoff = ksoff_full, voff[4], vsoff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) voff[i] = voff0 + i * vstride, vsoff[i] = vsoff0 + i * sstride;
+        uint32_t koff = koff_full, ksoff = ksoff_full;
         if (nv < kTile) { // wavefront-uniform: the wavefront's last tile
             const uint32_t tk = (uint32_t)(h < nv ? h : nv - 1);
             koff = tk * kstride + kq_off;
             ksoff = tk * sstride + ks_off;
-            vwin_offsets<D, VB>(4 * g, h, nv, vstride, sstride, voff, vsoff);
         }
         load_quarter<D, KB, true>(p.kc + row0 * KROW, reinterpret_cast<const uint8_t *>(p.ks + row0 * G),
                                   reinterpret_cast<const uint8_t *>(p.kz + row0 * G), koff, ksoff, kq);
-        load_vwin<D, VB>(p.vc + row0 * VROW, reinterpret_cast<const uint8_t *>(p.vs + row0 * G), voff, vsoff, h, vr);
     };
 
-    // one tile, from its loaded rows
-    auto tile = [&](int64_t t0, KQ &kq, const VRaw<D, VB> &vr) {
+    // one tile, from its loaded key rows
+    auto tile = [&](int64_t t0, KQ &kq, VRaw<D, VB> &vr) {
         const int nv = (int)(t_end - t0 < kTile ? t_end - t0 : kTile);
         finish_quarter<D, KB>(kq, g);
-        VW vw;
-        finish_vwin<D, VB>(vr, h, vw);
 
         // scores of the tile's 16 tokens
         float ksu[KQ::NG], kzs[KQ::NG];
@@ -535,6 +529,19 @@ __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, in
             }
         }
 
+        // the value windows are loaded only now, so that their registers are
+        // not held through the key contraction (four wavefronts per SIMD at
+        // d = 256)
+        {
+            const int64_t row0 = ((int64_t)b * p.width + t0) * p.hkv + j;
+            uint32_t voff[4], vsoff[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) voff[i] = voff0 + i * vstride, vsoff[i] = vsoff0 + i * sstride;
+            if (nv < kTile) vwin_offsets<D, VB>(4 * g, h, nv, vstride, sstride, voff, vsoff);
+            load_vwin<D, VB>(p.vc + row0 * VROW, reinterpret_cast<const uint8_t *>(p.vs + row0 * G), voff, vsoff, h, vr);
+        }
+        VW vw;
+        finish_vwin<D, VB>(vr, h, vw);
         // the first slice pair's value lookups, in flight during the softmax
         VLook look;
         value_lookup<D, VB>(vw, 0, tab, look);
@@ -602,7 +609,7 @@ __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, in
     for (int64_t t0 = t_lo; t0 < t_end; t0 += kTile) {
         KQ kq;
         VRaw<D, VB> vr;
-        load_tile(t0, kq, vr);
+        load_keys(t0, kq);
         tile(t0, kq, vr);
     }
 }
@@ -618,6 +625,12 @@ int64_t partial_lds_bytes(int d, int q_terms, int g)
     return query > merge ? query : merge;
 }
 
+// Register budget: four wavefronts per SIMD where the tile state fits in 128
+// VGPRs without spilling (every d <= 128; d = 256 below 8-bit codes); three
+// otherwise at d = 256; whatever d = 512 needs (its accumulators alone take
+// 128).
+template <int D, int VB, int KB> constexpr int kAttnWaves = D >= 512 ? 1 : (D == 256 && (VB == 8 || KB == 8)) ? 3 : 4;
+
 // Blocks are ordered so that the KV heads of one (sequence, chunk) are
 // dispatched to the same XCD one after another (dispatch deals block ids
 // to the 8 XCDs in turn): block id -> XCD x = id % 8, slot r = id / 8,
@@ -626,7 +639,8 @@ int64_t partial_lds_bytes(int d, int q_terms, int g)
 // wavefront of a block is an independent range of wave_tokens tokens (see
 // wave_tiles); the four are merged at the end of the block.
 template <int D, int VB, int KB, bool KS>
-__global__ void __launch_bounds__(kBlockThreads) attn_partial_kernel(AttnParams p)
+__global__ void __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(kAttnWaves<D, VB, KB>)))
+attn_partial_kernel(AttnParams p)
 {
     constexpr int NS = D / 16;  // output slices
     constexpr int W = D / 16;   // slice n holds dims W m + n

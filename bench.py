@@ -1,8 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the TurboQuant KV-cache codec on one MI355X.
 
-    python bench.py [--workload prefill|small_head|long_decode|joint_large]
-                    [--steps K] [--warmup W]
+    python bench.py [--workload NAME] [--steps K] [--warmup W]
 
 The default workload is the headline one, prefill: batch 1, 8 KV heads,
 head_dim 128, 32768 tokens, bf16 K/V with per-channel scales; values 4-bit
@@ -12,11 +11,19 @@ Lloyd-Max, keys 4-bit affine. What one step is:
                        then decode every token back to bf16 K and V; steps
                        rotate over enough independent buffer sets that a
                        step's data cannot stay in the 256 MB last-level cache;
+* prefill_encode,      the prefill encode alone, or the prefill decode alone
+  prefill_decode       (planes encoded beforehand), over rotating sets;
 * long_decode          append one token per head to a 131072-token cache
                        (encode 8 rows at the cache's end), then decode the
                        whole cache to bf16;
 * joint_large          one joint decode of packed K and V (262144 tokens x 8
                        heads, head_dim 512) to bf16;
+* long_k8v3            one joint decode of the ops page's long-sequence
+                       configuration (head_dim 256, K8 signed, V3, 32768
+                       tokens x 8 heads);
+* deferred_v           the long_decode cache decoded with values left in the
+                       rotated domain, then one 32-head attention output
+                       un-rotated (the eager decode timed alongside);
 * batch_merge          merge 32 packed caches of 4096..32768 tokens into one
                        left-padded batch (the token-axis batching
                        operation; KV tokens = tokens merged);
@@ -32,11 +39,14 @@ synchronisations, with HIP events on the launch stream at every kernel
 boundary. Prints one JSON line: value = KV tokens per second (one KV token
 = one position with K and V of all its heads; for the decode workloads,
 tokens decoded), the roofline of the dominant kernel (algorithmic bytes per
-launch / its average event-timed duration in the timed region, which
-includes the dispatch gap before it), the CPU oracle timed on the host as a
-baseline, and `graph_replay`: the same K steps captured in one HIP graph
-and replayed once after the timed region (no dispatch gaps; not for the
-Lloyd fit or the merge; --no-graph skips it). Diagnostics go to stderr.
+launch / its average duration: from the committed rocprofv3 trace of the
+workload under profiles/ when that trace was taken on the current sources,
+else from the events, which include the dispatch gap before the kernel;
+both are reported), HBM traffic from the committed counter runs under the
+same condition, the CPU oracle timed on the host as a baseline, and
+`graph_replay`: the same K steps captured in one HIP graph and replayed
+once after the timed region (no dispatch gaps; not for the Lloyd fit or
+the merge; --no-graph skips it). Diagnostics go to stderr.
 """
 from __future__ import annotations
 
@@ -69,6 +79,9 @@ DESCRIPTION = {
                    "cache to bf16",
     "joint_large": "joint_large: batch 4 x 65536 tokens, 8 KV heads, head_dim 512, bf16 N(0,1) with 1% of "
                    "rows zeroed; values 8-bit (unpacked bytes), keys 4-bit; one joint K/V decode to bf16",
+    "prefill_encode": "prefill_encode: the prefill inputs (batch 1, 8 KV heads, head_dim 128, 32768 tokens, bf16 "
+                      "K/V) encoded alone (values 4-bit, keys 4-bit), rotating over buffer sets so that the inputs "
+                      "are read from HBM",
     "prefill_decode": "prefill_decode: the prefill cache (batch 1, 8 KV heads, head_dim 128, 32768 tokens, values "
                       "4-bit, keys 4-bit) decoded to bf16 K and V alone, rotating over buffer sets so that the "
                       "packed planes are read from HBM",
@@ -92,6 +105,7 @@ METRIC = {
     "long_decode": "KV tokens/sec decoded per step (append 1 token + full decode, d=256, V5/K4) and "
                    "achieved HBM GB/s vs peak",
     "joint_large": "KV tokens/sec joint K/V decode (d=512, V8/K4) and achieved HBM GB/s vs peak",
+    "prefill_encode": "KV tokens/sec encode alone (d=128, V4/K4, bf16 inputs from HBM) and achieved HBM GB/s vs peak",
     "prefill_decode": "KV tokens/sec decode alone (d=128, 4-bit, planes from HBM) and achieved HBM GB/s vs peak",
     "long_k8v3": "KV tokens/sec joint K/V decode (d=256, K8 signed, V3, 32768 tokens) and achieved HBM GB/s vs peak",
     "deferred_v": "KV tokens/sec decoded with deferred value un-rotation (d=256, V5/K4) and achieved HBM GB/s vs "
@@ -409,6 +423,33 @@ def setup_decode_only(torch, tq, W, w, dev, sets_hint):
         {**codec_config(w), "workload": DESCRIPTION[w.name], "buffer_sets": nsets}
 
 
+def setup_encode_only(torch, tq, W, w, dev, sets_hint):
+    """Encode alone, rotating over buffer sets of K/V inputs and planes, so
+    that each step reads its inputs from HBM and no decode's output is being
+    written back meanwhile."""
+    k0, v0 = W.make_kv(w, dev)
+    enc_b, _ = row_bytes(w)
+    per_set = w.rows * enc_b
+    nsets = sets_hint or max(2, math.ceil(1.5 * 2 ** 30 / per_set))
+    sets = []
+    for s in range(nsets):
+        k = k0 if s == 0 else k0.clone()
+        v = v0 if s == 0 else v0.clone()
+        sets.append((k, v, tq.empty_planes(w.rows, w.head_dim, w.k_bits, w.v_bits, dev)))
+    torch.cuda.synchronize()
+    log(f"workload {w.name}: {w.rows} rows, {nsets} buffer sets of {per_set / 2**20:.0f} MiB (inputs + planes)")
+
+    def step(i, ev=None):
+        k, v, planes = sets[i % nsets]
+        if ev is not None:
+            ev[0].record()
+        tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed, out=planes)
+
+    cpu = lambda: cpu_baseline(w, W.to_oracle(k0), W.to_oracle(v0), True, False, 1.0 / w.heads)
+    return step, 1, {"encode": (0, 1, w.rows * enc_b)}, (lambda i: w.kv_tokens), cpu, \
+        {**codec_config(w), "workload": DESCRIPTION[w.name], "buffer_sets": nsets}
+
+
 def setup_deferred_v(torch, tq, W, dev, steps_total):
     """Rotated-domain value decode plus one un-rotation of an attention
     output per step; the eager decode (inverse transform for every token) of
@@ -647,11 +688,16 @@ def main():
     w = W.WORKLOADS.get(args.workload)
     steps = args.steps or {"long_decode": 20, "joint_large": 20, "batch_merge": 20, "lloyd_fit": 3,
                            "attn_decode": 50, "deferred_v": 20, "long_k8v3": 50,
-                           "prefill_decode": 50}.get(args.workload, 50)
+                           "prefill_decode": 50, "prefill_encode": 50}.get(args.workload, 50)
 
     extra = None
     if args.workload in ("prefill", "small_head"):
         step, marks, kernels, tokens, cpu_fn, config = setup_encode_decode(torch, tq, W, w, dev, args.sets)
+    elif args.workload == "prefill_encode":
+        w = W.WORKLOADS["prefill"]
+        w = W.Workload("prefill_encode", w.batch, w.tokens, w.heads, w.head_dim, w.dtype, w.v_bits, w.k_bits,
+                       w.k_signed, w.seed, w.kind)
+        step, marks, kernels, tokens, cpu_fn, config = setup_encode_only(torch, tq, W, w, dev, args.sets)
     elif args.workload == "prefill_decode":
         w = W.WORKLOADS["prefill"]
         w = W.Workload("prefill_decode", w.batch, w.tokens, w.heads, w.head_dim, w.dtype, w.v_bits, w.k_bits,

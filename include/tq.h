@@ -268,7 +268,10 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
  * launch) when tq_attention_workspace_bytes() for the call exceeds 64 MiB.
  * All calls on one GPU share its buffer and each call leaves its partials
  * there: calls that may overlap on one GPU (concurrent streams, or host
- * threads) race and must be ordered by the caller. */
+ * threads) race and must be ordered by the caller. The first call on a
+ * device with width > 0 looks up the buffer's device address (a runtime
+ * query, not an allocation); callers that capture graphs make that first
+ * call outside the capture. */
 int32_t tq_attention_decode_static(const void *q, int32_t q_dtype, const tq_packed_kv *cache, int32_t batch,
                                    int64_t width, const int32_t *left_pad, int32_t kv_heads, int32_t q_heads,
                                    const tq_config *cfg, float scale, void *out, int32_t out_dtype, void *stream);

@@ -48,3 +48,45 @@ def test_static_scratch_attention_equals_workspace_entry_point():
     one_case(2, 9000, 8, 32, 256, 4, 5, False, torch.bfloat16, torch.float32, [0, 1234], seed=101)
     print("[no-alloc] call 2: batch 1, width 700, 2 KV heads, 8 query heads, d=128, V3/K8s, bf16 out", flush=True)
     one_case(1, 700, 2, 8, 128, 8, 3, True, torch.float32, torch.bfloat16, None, seed=202)
+
+
+def test_static_attention_replays_in_a_hip_graph():
+    """The use it exists for: the allocation-free call captured in a HIP
+    graph (stream capture on a stream of its own) and replayed three times,
+    with eager calls of the same entry point on another query in between
+    (they overwrite the shared static buffer); every replay must reproduce
+    the workspace entry point's output bit for bit. One eager call comes
+    first: the first call on a device looks up the buffer's address."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_quantization_tq_amd.hiprt import HipGraph
+
+    tq.lib()
+    T, H, hq, d, kb, vb = 5000, 4, 16, 256, 4, 5
+    print(f"[no-alloc] graph: width {T}, {H} KV heads, {hq} query heads, d={d}, V{vb}/K{kb}", flush=True)
+    k = randn((T, H, d), torch.bfloat16, 301)
+    v = randn((T, H, d), torch.bfloat16, 302)
+    cache = tq.encode_kv(k, v, v_bits=vb, k_bits=kb)
+    q, q2 = randn((1, hq, d), torch.bfloat16, 303), randn((1, hq, d), torch.bfloat16, 304)
+    args = dict(batch=1, width=T, kv_heads=H, head_dim=d, k_bits=kb, v_bits=vb)
+    ws = torch.empty(int(tq.lib().tq_attention_workspace_bytes(1, H, hq, d, T)), dtype=torch.uint8, device=DEV)
+    ref = tq.attention_decode(q, cache, workspace=ws, **args)
+    ref2 = tq.attention_decode(q2, cache, workspace=ws, **args)
+    out, out2 = torch.empty_like(ref), torch.empty_like(ref)
+    tq.attention_decode_static(q, cache, out=out, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    graph = HipGraph(torch, lambda: tq.attention_decode_static(q, cache, out=out, **args))
+    try:
+        for r in range(3):
+            out.zero_()
+            out2.zero_()
+            tq.attention_decode_static(q2, cache, out=out2, **args)
+            torch.cuda.synchronize()
+            assert torch.equal(out2.view(torch.int32), ref2.view(torch.int32)), f"eager call before replay {r}"
+            graph.launch()
+            graph.synchronize()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {r}"
+    finally:
+        graph.close()

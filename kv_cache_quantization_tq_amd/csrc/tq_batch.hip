@@ -14,6 +14,8 @@
 // kernel performs a list of segments.
 #include <hip/hip_runtime.h>
 
+#include <stdint.h>
+
 #include <algorithm>
 #include <vector>
 
@@ -132,15 +134,27 @@ int32_t check_src(const tq_packed_kv *src, const tq_packed_kv *dst)
     return TQ_OK;
 }
 
-// Collects segments and launches them in batches of kMaxSegs.
+// Collects segments and launches them in batches of kMaxSegs. Every
+// segment is checked against the extents of its source and destination
+// (in tokens, as the call's arguments define them); a call that would build
+// one outside them launches nothing and returns TQ_E_SHAPE.
 class Segments {
   public:
-    // copy `tokens` tokens from src token s0 to dst token d0 (src NULL:
-    // zero-fill), in every plane dst has
-    void add(const tq_packed_kv *src, int64_t s0, const tq_packed_kv *dst, int64_t d0, int64_t tokens,
-             const int64_t tb[kPlanes])
+    // copy `tokens` tokens from src token s0 (of src_tokens) to dst token d0
+    // (of dst_tokens) (src NULL: zero-fill), in every plane dst has
+    void add(const tq_packed_kv *src, int64_t s0, int64_t src_tokens, const tq_packed_kv *dst, int64_t d0,
+             int64_t dst_tokens, int64_t tokens, const int64_t tb[kPlanes])
     {
         if (tokens <= 0) return;
+        if (d0 < 0 || d0 > dst_tokens - tokens || (src != nullptr && (s0 < 0 || s0 > src_tokens - tokens))) {
+            outside_ = true;
+            return;
+        }
+        for (int i = 0; i < kPlanes; ++i)
+            if (tb[i] > 0 && tokens > INT64_MAX / tb[i]) {
+                outside_ = true;
+                return;
+            }
         uint8_t *s[kPlanes] = {nullptr, nullptr, nullptr, nullptr, nullptr}, *d[kPlanes];
         if (src != nullptr) plane_ptrs(src, s);
         plane_ptrs(dst, d);
@@ -152,6 +166,7 @@ class Segments {
 
     int32_t launch(void *stream) const
     {
+        if (outside_) return TQ_E_SHAPE;
         // A graph replay of calls making several launches each faulted on
         // MI355X (cause not established): such calls refuse capture before
         // launching anything.
@@ -181,6 +196,7 @@ class Segments {
 
   private:
     std::vector<Seg> segs_;
+    bool outside_ = false;
 };
 
 bool token_count_ok(int64_t t) { return t >= 0 && t <= ((int64_t)1 << 40); }
@@ -221,8 +237,8 @@ int32_t tq_merge_rows(const tq_packed_kv *srcs, const int64_t *lens, int32_t n, 
     Segments sg;
     for (int32_t i = 0; i < n; ++i) {
         const int64_t pad = width - lens[i];
-        sg.add(nullptr, 0, dst, i * width, pad, tb);
-        sg.add(&srcs[i], 0, dst, i * width + pad, lens[i], tb);
+        sg.add(nullptr, 0, 0, dst, i * width, (int64_t)n * width, pad, tb);
+        sg.add(&srcs[i], 0, lens[i], dst, i * width + pad, (int64_t)n * width, lens[i], tb);
     }
     if ((st = sg.launch(stream)) != TQ_OK) return st;
     if (left_pad != nullptr)
@@ -252,12 +268,13 @@ int32_t tq_extend_rows(const tq_packed_kv *batch, int32_t b, int64_t width, cons
     const int64_t shift = new_width - width;
     if (new_width > 0) {
         Segments sg;
+        const int64_t out_tokens = (int64_t)(b + 1) * new_width, in_tokens = (int64_t)b * width;
         for (int32_t i = 0; i < b; ++i) {
-            sg.add(nullptr, 0, dst, i * new_width, shift, tb);
-            sg.add(batch, i * width, dst, i * new_width + shift, width, tb);
+            sg.add(nullptr, 0, 0, dst, i * new_width, out_tokens, shift, tb);
+            sg.add(batch, i * width, in_tokens, dst, i * new_width + shift, out_tokens, width, tb);
         }
-        sg.add(nullptr, 0, dst, (int64_t)b * new_width, new_width - row_len, tb);
-        sg.add(row, 0, dst, (int64_t)b * new_width + new_width - row_len, row_len, tb);
+        sg.add(nullptr, 0, 0, dst, (int64_t)b * new_width, out_tokens, new_width - row_len, tb);
+        sg.add(row, 0, row_len, dst, (int64_t)b * new_width + new_width - row_len, out_tokens, row_len, tb);
         if ((st = sg.launch(stream)) != TQ_OK) return st;
     }
     if (left_pad_out != nullptr) {
@@ -278,7 +295,7 @@ int32_t tq_extract_row(const tq_packed_kv *batch, int32_t b, int64_t width, int3
     if (st != TQ_OK) return st;
     if ((st = check_src(batch, dst)) != TQ_OK) return st;
     Segments sg;
-    sg.add(batch, (int64_t)i * width + left_pad, dst, 0, width - left_pad, tb);
+    sg.add(batch, (int64_t)i * width + left_pad, (int64_t)b * width, dst, 0, width - left_pad, width - left_pad, tb);
     return sg.launch(stream);
 }
 
@@ -296,7 +313,9 @@ int32_t tq_filter_rows(const tq_packed_kv *batch, int32_t b, int64_t width, cons
     if (st != TQ_OK) return st;
     if ((st = check_src(batch, dst)) != TQ_OK) return st;
     Segments sg;
-    for (int32_t j = 0; j < n; ++j) sg.add(batch, (int64_t)keep[j] * width, dst, (int64_t)j * width, width, tb);
+    for (int32_t j = 0; j < n; ++j)
+        sg.add(batch, (int64_t)keep[j] * width, (int64_t)b * width, dst, (int64_t)j * width, (int64_t)n * width, width,
+               tb);
     return sg.launch(stream);
 }
 

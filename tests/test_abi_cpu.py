@@ -245,6 +245,48 @@ def test_batching_argument_validation():
     assert L.tq_filter_rows(by(dst), 2, 5, None, 0, 2, by(cfg), by(dst), None) == tq.TQ_OK
 
 
+def test_batching_segments_stay_inside_their_planes():
+    """Every copy segment a batching call builds is checked against the
+    extents of its source and destination planes (in tokens, from the call's
+    arguments) before anything is launched: one outside returns TQ_E_SHAPE.
+    Without a GPU the launch itself fails (TQ_E_HIP), so reaching it means
+    every segment of the call passed. Driven here with the merge of 32
+    caches that the bench times (three launches of segments), and extend,
+    extract and filter shapes around it; plane pointers are never
+    dereferenced on the host."""
+    import numpy as np
+    from kv_cache_quantization_tq_amd import workloads as W
+    L = tq.lib()
+    by = ctypes.byref
+    m = W.MERGE
+    lens = W.merge_lengths()
+    n, width, H = len(lens), max(lens), m["heads"]
+    cfg = tq.TQConfig(m["head_dim"], m["k_bits"], m["v_bits"], 0)
+    srcs = (tq.TQPackedKV * n)(*[_pk([FAKE + 4096 * i] * 5) for i in range(n)])
+    lens_a = np.asarray(lens, dtype=np.int64)
+    dst = _pk([FAKE] * 5)
+    pads = np.zeros(n, dtype=np.int64)
+    assert L.tq_merge_rows(srcs, lens_a.ctypes.data, n, width, H, by(cfg), by(dst), pads.ctypes.data,
+                           None) == tq.TQ_E_HIP
+    # ragged shapes: empty, full and one-token sequences; values-only planes
+    for ls in ([0, 1, 7], [5, 5, 5], [1], [0, 0, 3]):
+        la = np.asarray(ls, dtype=np.int64)
+        ss = (tq.TQPackedKV * len(ls))(*[_pk([FAKE] * 5) for _ in ls])
+        for d in (dst, _pk([None, None, None, FAKE, FAKE])):
+            assert L.tq_merge_rows(ss, la.ctypes.data, len(ls), max(ls), 2, by(cfg), by(d), None,
+                                   None) == tq.TQ_E_HIP, ls
+    pin = (ctypes.c_int64 * 3)(0, 2, 5)
+    pout = (ctypes.c_int64 * 4)()
+    row = _pk([FAKE] * 5)
+    for b, w, rl, nw in ((3, 5, 5, 5), (3, 5, 2, 9), (0, 0, 4, 4), (3, 5, 0, 6)):
+        assert L.tq_extend_rows(by(dst), b, w, pin, by(row), rl, nw, 2, by(cfg), by(dst), pout,
+                                None) == tq.TQ_E_HIP, (b, w, rl, nw)
+    for i, pad in ((0, 0), (2, 4), (1, 3)):
+        assert L.tq_extract_row(by(dst), 3, 5, i, pad, 2, by(cfg), by(dst), None) == tq.TQ_E_HIP
+    keep = (ctypes.c_int32 * 4)(2, 0, 2, 1)
+    assert L.tq_filter_rows(by(dst), 3, 5, keep, 4, 2, by(cfg), by(dst), None) == tq.TQ_E_HIP
+
+
 def test_lloyd_fit_argument_validation():
     import numpy as np
     L = tq.lib()

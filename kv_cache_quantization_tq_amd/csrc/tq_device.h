@@ -987,10 +987,17 @@ __device__ __forceinline__ void encode_loop(const void *__restrict__ kin, const 
     }
 }
 
+// Wavefronts per SIMD asked of the register allocator: five where the
+// encoder's state fits in 96 VGPRs without spilling (bf16 inputs, every value
+// width but 3 bits up to head_dim 128, 2- and 8-bit values above; one more
+// wavefront in flight hides more of the loads' latency), else no constraint
+// (1). TQ_ENCODE_WAVES, when defined, overrides it for every configuration.
+template <int D, int VB, bool BF16IN>
+constexpr int kEncodeWaves = BF16IN && VB != 3 && (D <= 128 || VB == 8 || (D == 256 && VB == 2)) ? 5 : 1;
 #if TQ_ENCODE_WAVES > 0
 #define TQ_ENCODE_ATTR __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(TQ_ENCODE_WAVES)))
 #else
-#define TQ_ENCODE_ATTR __launch_bounds__(kBlockThreads)
+#define TQ_ENCODE_ATTR __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(kEncodeWaves<D, VB, BF16IN>)))
 #endif
 
 template <int D, int VB, bool BF16IN>

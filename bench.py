@@ -35,17 +35,19 @@ Lloyd-Max, keys 4-bit affine. What one step is:
 
 Inputs are resident in HBM before timing starts. The timed region is
 exactly K steps launched one by one after W warm-up steps, bracketed by
-synchronisations, with HIP events on the launch stream at every kernel
-boundary. Prints one JSON line: value = KV tokens per second (one KV token
-= one position with K and V of all its heads; for the decode workloads,
-tokens decoded), the roofline of the dominant kernel (algorithmic bytes per
-launch / its average duration: from the committed rocprofv3 trace of the
-workload under profiles/ when that trace was taken on the current sources,
-else from the events, which include the dispatch gap before the kernel;
-both are reported), HBM traffic from the committed counter runs under the
-same condition, the CPU oracle timed on the host as a baseline, and
+synchronisations and two HIP events on the launch stream (the step time);
+every kernel call in it is timed by a pair of HIP events that the library
+binds to the start of its first and the end of its last dispatch
+(tq_time_next_call), i.e. device time, as a kernel trace measures it.
+Prints one JSON line: value = KV tokens per second (one KV token = one
+position with K and V of all its heads; for the decode workloads, tokens
+decoded), the roofline of the dominant kernel (algorithmic bytes per
+launch / its average event-timed duration; beside it the committed
+rocprofv3 trace of the workload under profiles/ when that trace was taken
+on the current sources), HBM traffic from the committed counter runs under
+the same condition, the CPU oracle timed on the host as a baseline, and
 `graph_replay`: the same K steps captured in one HIP graph and replayed
-once after the timed region (no dispatch gaps; not for the Lloyd fit or
+once after the timed region (one submission for all kernels; not for the Lloyd fit or
 the merge; --no-graph skips it). Diagnostics go to stderr.
 """
 from __future__ import annotations
@@ -266,31 +268,26 @@ def cpu_baseline(w, kn, vn, do_encode, do_decode, tokens_per_row):
 # ---------------------------------------------------------------------------
 
 class Timer:
-    """Events on the launch stream over the timed loop: ev[i][0] marks the
-    start of step i (and the end of step i - 1), ev[i][m] for m >= 1 the
-    boundaries between the step's kernels; ev[steps][0] ends the loop. A
-    kernel is a pair (a, b) of mark indices, b == marks meaning the next
-    step's start."""
+    """Timing of the timed loop: a pair of HIP events around the whole loop
+    (the step time), and per step and kernel a start/stop pair that the
+    library binds to that kernel's own dispatch (tq_time_next_call), so that
+    a kernel's figure is its device time from start to end, the interval a
+    kernel trace reports."""
 
-    def __init__(self, torch, steps, marks):
+    def __init__(self, torch, steps, names):
         stream = ctypes_stream(torch)
-        self.marks = marks
-        self.ev = [[HipEvent(stream) for _ in range(marks)] for _ in range(steps)] + [[HipEvent(stream)]]
+        self.start, self.end = HipEvent(stream), HipEvent(stream)
+        self.ev = [{n: (HipEvent(stream), HipEvent(stream)) for n in names} for _ in range(steps)]
 
-    @property
-    def start(self):
-        return self.ev[0][0]
+    def per_kernel_ms(self, name):
+        return [a.elapsed_time(b) for a, b in (row[name] for row in self.ev)]
 
-    @property
-    def end(self):
-        return self.ev[-1][0]
 
-    def per_kernel_ms(self, a, b):
-        out = []
-        for i in range(len(self.ev) - 1):
-            e1 = self.ev[i + 1][0] if b == self.marks else self.ev[i][b]
-            out.append(self.ev[i][a].elapsed_time(e1))
-        return out
+def arm(tq, ev, name):
+    """Bind the step's event pair for `name` to the kernels of the next
+    library call (no-op outside the timed loop)."""
+    if ev is not None:
+        tq.time_next_call(*ev[name])
 
 
 def ctypes_stream(torch):
@@ -315,19 +312,17 @@ def setup_encode_decode(torch, tq, W, w, dev, sets_hint):
 
     def step(i, ev=None):
         k, v, planes, ko, vo = sets[i % nsets]
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "encode")
         tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed, out=planes)
-        if ev is not None:
-            ev[1].record()
+        arm(tq, ev, "decode")
         tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
                      k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
 
     enc_b, dec_b = row_bytes(w)
-    kernels = {"encode": (0, 1, w.rows * enc_b), "decode": (1, 2, w.rows * dec_b)}
+    kernels = {"encode": w.rows * enc_b, "decode": w.rows * dec_b}
     tokens = lambda i: w.kv_tokens
     cpu = lambda: cpu_baseline(w, W.to_oracle(k0), W.to_oracle(v0), True, True, 1.0 / w.heads)
-    return step, 2, kernels, tokens, cpu, {**codec_config(w), "buffer_sets": nsets}
+    return step, kernels, tokens, cpu, {**codec_config(w), "buffer_sets": nsets}
 
 
 def setup_long_decode(torch, tq, W, w, dev, max_steps):
@@ -350,21 +345,19 @@ def setup_long_decode(torch, tq, W, w, dev, max_steps):
         n = T + i  # tokens already cached
         view = {nm: p[n * H:(n + 1) * H] for nm, p in planes.items()}
         nk, nv = appends[i]
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "append")
         tq.encode_kv(nk, nv, v_bits=w.v_bits, k_bits=w.k_bits, out=view)
-        if ev is not None:
-            ev[1].record()
+        arm(tq, ev, "decode")
         tq.decode_kv(planes, tokens=n + 1, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits,
                      k_out=ko[: n + 1], v_out=vo[: n + 1])
 
     enc_b, dec_b = row_bytes(w)
     # decode bytes of the first timed step's cache length (the cache grows by
     # one token per step: under 0.05% over a run)
-    kernels = {"append": (0, 1, H * enc_b), "decode": (1, 2, (T + 1) * H * dec_b)}
+    kernels = {"append": H * enc_b, "decode": (T + 1) * H * dec_b}
     tokens = lambda i: T + i + 1
     cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
-    return step, 2, kernels, tokens, cpu, {**codec_config(w), "cached_tokens": T, "appended_per_step": 1}
+    return step, kernels, tokens, cpu, {**codec_config(w), "cached_tokens": T, "appended_per_step": 1}
 
 
 def setup_joint(torch, tq, W, w, dev):
@@ -379,14 +372,13 @@ def setup_joint(torch, tq, W, w, dev):
     log(f"workload {w.name}: {w.rows} rows")
 
     def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "decode")
         tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
                      k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
 
     _, dec_b = row_bytes(w)
     cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
-    return step, 1, {"decode": (0, 1, w.rows * dec_b)}, (lambda i: w.kv_tokens), cpu, codec_config(w)
+    return step, {"decode": w.rows * dec_b}, (lambda i: w.kv_tokens), cpu, codec_config(w)
 
 
 def codec_config(w):
@@ -413,13 +405,12 @@ def setup_decode_only(torch, tq, W, w, dev, sets_hint):
 
     def step(i, ev=None):
         planes, ko, vo = sets[i % nsets]
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "decode")
         tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
                      k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
 
     cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
-    return step, 1, {"decode": (0, 1, w.rows * dec_b)}, (lambda i: w.kv_tokens), cpu, \
+    return step, {"decode": w.rows * dec_b}, (lambda i: w.kv_tokens), cpu, \
         {**codec_config(w), "workload": DESCRIPTION[w.name], "buffer_sets": nsets}
 
 
@@ -441,12 +432,11 @@ def setup_encode_only(torch, tq, W, w, dev, sets_hint):
 
     def step(i, ev=None):
         k, v, planes = sets[i % nsets]
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "encode")
         tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed, out=planes)
 
     cpu = lambda: cpu_baseline(w, W.to_oracle(k0), W.to_oracle(v0), True, False, 1.0 / w.heads)
-    return step, 1, {"encode": (0, 1, w.rows * enc_b)}, (lambda i: w.kv_tokens), cpu, \
+    return step, {"encode": w.rows * enc_b}, (lambda i: w.kv_tokens), cpu, \
         {**codec_config(w), "workload": DESCRIPTION[w.name], "buffer_sets": nsets}
 
 
@@ -471,26 +461,24 @@ def setup_deferred_v(torch, tq, W, dev, steps_total):
     log(f"workload deferred_v: {T} tokens x {H} heads, rotated decode + un-rotation of {hq} rows")
 
     def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "decode")
         tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo,
                      rotated_v=True)
-        if ev is not None:
-            ev[1].record()
+        arm(tq, ev, "unrotate")
         tq.unrotate_values(att, out=att_out)
 
     def eager_us(reps=20):
-        """Average event time of the eager decode (values fully decoded)."""
-        ev = [HipEvent(ctypes_stream(torch)) for _ in range(reps + 1)]
+        """Average device time of the eager decode (values fully decoded),
+        timed like the kernels of the timed loop."""
+        ev = [(HipEvent(ctypes_stream(torch)), HipEvent(ctypes_stream(torch))) for _ in range(reps)]
         for _ in range(3):
             tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo)
         torch.cuda.synchronize()
-        ev[0].record()
-        for i in range(reps):
+        for a, b in ev:
+            tq.time_next_call(a, b)
             tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo)
-            ev[i + 1].record()
         torch.cuda.synchronize()
-        return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps * 1e3
+        return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
 
     def cpu():
         import oracle as O
@@ -521,9 +509,9 @@ def setup_deferred_v(torch, tq, W, dev, steps_total):
                           f"over {nt} threads (single-thread figure alongside)"}
 
     _, dec_b = row_bytes(w)
-    kernels = {"decode": (0, 1, T * H * dec_b), "unrotate": (1, 2, 2 * hq * d * 4)}
+    kernels = {"decode": T * H * dec_b, "unrotate": 2 * hq * d * 4}
     config = {**codec_config(w), "workload": DESCRIPTION["deferred_v"], "q_heads": hq, "rotated_v": True}
-    return step, 2, kernels, (lambda i: T), cpu, config, eager_us
+    return step, kernels, (lambda i: T), cpu, config, eager_us
 
 
 def setup_batch_merge(torch, tq, W, dev):
@@ -546,8 +534,7 @@ def setup_batch_merge(torch, tq, W, dev):
     pk = _packed(dst)
 
     def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "merge")
         st = tq.lib().tq_merge_rows(srcs, lens_a.ctypes.data, len(lens), width, H, ctypes.byref(cfg),
                                     ctypes.byref(pk), None, ctypes_stream(torch))
         if st:
@@ -567,7 +554,7 @@ def setup_batch_merge(torch, tq, W, dev):
 
     config = {"workload": DESCRIPTION["batch_merge"], "sequences": len(lens), "tokens": sum(lens), "width": width,
               "heads": H, "head_dim": d, "v_bits": vb, "k_bits": kb}
-    return step, 1, {"merge": (0, 1, nbytes)}, (lambda i: sum(lens)), cpu, config
+    return step, {"merge": nbytes}, (lambda i: sum(lens)), cpu, config
 
 
 def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
@@ -581,8 +568,7 @@ def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
     log(f"workload lloyd_fit: {n} samples, {levels} levels, {iterations} iterations per step")
 
     def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "fit")
         tq.lloyd_max_fit(x, levels, init, iterations, workspace=ws)
 
     def cpu():
@@ -604,7 +590,7 @@ def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
     # int64 prefix sums (12n). The iterations read a few windows of keys and
     # sums per boundary each and are bound by their dependent latency, not by
     # bandwidth.
-    return step, 1, {"fit": (0, 1, 48 * n)}, (lambda i: n * iterations), cpu, config
+    return step, {"fit": 48 * n}, (lambda i: n * iterations), cpu, config
 
 
 def setup_attn_decode(torch, tq, W, dev):
@@ -627,8 +613,7 @@ def setup_attn_decode(torch, tq, W, dev):
     log(f"workload attn_decode: {T} tokens x {H} KV heads, {hq} query heads, {T * H * row_b / 1e6:.1f} MB of cache")
 
     def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
+        arm(tq, ev, "attention")
         tq.attention_decode(q, planes, batch=1, width=T, kv_heads=H, head_dim=d, k_bits=w.k_bits,
                             v_bits=w.v_bits, out=out, workspace=ws)
 
@@ -651,7 +636,7 @@ def setup_attn_decode(torch, tq, W, dev):
 
     config = {"workload": DESCRIPTION["attn_decode"], "tokens": T, "kv_heads": H, "q_heads": hq, "head_dim": d,
               "v_bits": w.v_bits, "k_bits": w.k_bits, "q_dtype": "bf16"}
-    return step, 1, {"attention": (0, 1, nbytes)}, (lambda i: T), cpu, config
+    return step, {"attention": nbytes}, (lambda i: T), cpu, config
 
 
 def main():
@@ -692,34 +677,34 @@ def main():
 
     extra = None
     if args.workload in ("prefill", "small_head"):
-        step, marks, kernels, tokens, cpu_fn, config = setup_encode_decode(torch, tq, W, w, dev, args.sets)
+        step, kernels, tokens, cpu_fn, config = setup_encode_decode(torch, tq, W, w, dev, args.sets)
     elif args.workload == "prefill_encode":
         w = W.WORKLOADS["prefill"]
         w = W.Workload("prefill_encode", w.batch, w.tokens, w.heads, w.head_dim, w.dtype, w.v_bits, w.k_bits,
                        w.k_signed, w.seed, w.kind)
-        step, marks, kernels, tokens, cpu_fn, config = setup_encode_only(torch, tq, W, w, dev, args.sets)
+        step, kernels, tokens, cpu_fn, config = setup_encode_only(torch, tq, W, w, dev, args.sets)
     elif args.workload == "prefill_decode":
         w = W.WORKLOADS["prefill"]
         w = W.Workload("prefill_decode", w.batch, w.tokens, w.heads, w.head_dim, w.dtype, w.v_bits, w.k_bits,
                        w.k_signed, w.seed, w.kind)
-        step, marks, kernels, tokens, cpu_fn, config = setup_decode_only(torch, tq, W, w, dev, args.sets)
+        step, kernels, tokens, cpu_fn, config = setup_decode_only(torch, tq, W, w, dev, args.sets)
     elif args.workload == "long_k8v3":
-        step, marks, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
+        step, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
         config["workload"] = DESCRIPTION["long_k8v3"]
     elif args.workload == "deferred_v":
-        step, marks, kernels, tokens, cpu_fn, config, extra = setup_deferred_v(torch, tq, W, dev,
+        step, kernels, tokens, cpu_fn, config, extra = setup_deferred_v(torch, tq, W, dev,
                                                                                args.warmup + steps)
     elif args.workload == "long_decode":
-        step, marks, kernels, tokens, cpu_fn, config = setup_long_decode(torch, tq, W, w, dev,
+        step, kernels, tokens, cpu_fn, config = setup_long_decode(torch, tq, W, w, dev,
                                                                          args.warmup + steps)
     elif args.workload == "joint_large":
-        step, marks, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
+        step, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
     elif args.workload == "batch_merge":
-        step, marks, kernels, tokens, cpu_fn, config = setup_batch_merge(torch, tq, W, dev)
+        step, kernels, tokens, cpu_fn, config = setup_batch_merge(torch, tq, W, dev)
     elif args.workload == "lloyd_fit":
-        step, marks, kernels, tokens, cpu_fn, config = setup_lloyd_fit(torch, tq, W, dev)
+        step, kernels, tokens, cpu_fn, config = setup_lloyd_fit(torch, tq, W, dev)
     else:
-        step, marks, kernels, tokens, cpu_fn, config = setup_attn_decode(torch, tq, W, dev)
+        step, kernels, tokens, cpu_fn, config = setup_attn_decode(torch, tq, W, dev)
     torch.cuda.synchronize()
 
     if args.copy_calibration_mib:
@@ -736,11 +721,12 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # the timed region: exactly `steps` steps launched one by one, with
-    # events on the launch stream at every kernel boundary (each kernel's
-    # figure includes the dispatch between it and the previous launch)
-    tm = Timer(torch, steps, marks)
+    # the timed region: exactly `steps` steps launched one by one between
+    # two events on the launch stream, each kernel timed by events bound to
+    # its own dispatch
+    tm = Timer(torch, steps, kernels)
     torch.cuda.synchronize()
+    tm.start.record()
     for i in range(steps):
         step(args.warmup + i, tm.ev[i])
     tm.end.record()
@@ -749,7 +735,7 @@ def main():
     kv_tokens = sum(tokens(args.warmup + i) for i in range(steps))
 
     # reported alongside: the same `steps` steps captured in one graph and
-    # replayed once (one submission for all their kernels, no dispatch gaps),
+    # replayed once (one submission for all their kernels),
     # after an untimed replay that uploads the graph. Not for the Lloyd fit,
     # which reads its result back to the host every step, nor the merge,
     # whose graph replay faulted (its launches carry 2.9 KB segment lists as
@@ -772,15 +758,15 @@ def main():
             f"(timed region, launched one by one: {ms_per_step * 1e3:.1f} us)")
 
     stats = {}
-    for name, (a, b, nbytes) in kernels.items():
-        ms = sorted(tm.per_kernel_ms(a, b))
+    for name, nbytes in kernels.items():
+        ms = sorted(tm.per_kernel_ms(name))
         avg = sum(ms) / len(ms)
         gbps = nbytes / (avg * 1e-3) / 1e9
         stats[name] = {"avg_us": avg * 1e3, "median_us": ms[len(ms) // 2] * 1e3, "GBps": gbps,
                        "bytes": nbytes, "frac": gbps / PEAK_HBM_GBPS}
         log(f"{name}: avg {avg * 1e3:.1f} us  median {ms[len(ms) // 2] * 1e3:.1f} us  "
             f"{gbps:.0f} GB/s ({gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s)")
-    step_bytes = sum(v[2] for v in kernels.values())
+    step_bytes = sum(kernels.values())
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     copy_gbps = device_copy_gbps(torch, dev)
     log(f"step: {ms_per_step * 1e3:.1f} us, {step_gbps:.0f} GB/s ({step_gbps / PEAK_HBM_GBPS:.1%} of 8 TB/s); "
@@ -796,7 +782,7 @@ def main():
             f"{stats['decode']['avg_us']:.1f} us + un-rotation {stats['unrotate']['avg_us']:.1f} us")
     cpu = None if args.no_cpu_baseline else cpu_fn()
     # the committed kernel trace of this workload on the same sources, beside
-    # the live event figures (which include the dispatch gap before a kernel)
+    # the live event figures
     tr = committed_trace(args.workload, kernel_kind_of(dom))
     trace_fields = None if tr is None else {
         "source": f"profiles/{args.workload}_kernel_trace.json", "avg_us": tr["avg_us"],

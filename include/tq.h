@@ -66,8 +66,9 @@ enum {
     TQ_E_DTYPE = 5,    /* dtype not TQ_F32 / TQ_BF16                          */
     TQ_E_SHAPE = 6,    /* negative tokens, heads < 1, or row count overflow   */
     TQ_E_HIP = 7,      /* the HIP runtime reported an error at launch         */
-    TQ_E_CAPTURE = 8,  /* a batching call needing more than one launch was    */
-                       /* made on a stream that is capturing a graph          */
+    TQ_E_CAPTURE = 8,  /* a batching call needing more than one launch, or a  */
+                       /* call with kernel timing armed, was made on a stream */
+                       /* that is capturing a graph                           */
     TQ_E_SCRATCH = 9   /* the call needs more scratch than the library's      */
                        /* static buffer holds                                 */
 };
@@ -109,6 +110,22 @@ int64_t tq_packed_dim(int32_t dim, int32_t bits);
 
 /* Static, NUL-terminated message for a status code (never NULL). */
 const char *tq_status_string(int32_t status);
+
+/* Kernel timing, for callers that measure the kernels (benchmarks): not an
+ * operation of the pages. Arms the calling host thread so that the next
+ * call of this library that takes a `stream` binds `start` to the start of
+ * the first kernel it launches and `stop` to the end of the last one
+ * (hipExtLaunchKernel's start and stop events). hipEventElapsedTime(start,
+ * stop) then gives the device time from the first kernel's start to the
+ * last kernel's end, without the dispatch ahead of the first kernel that an
+ * event recorded before the call would include. `start` and `stop` are
+ * hipEvent_t handles created and owned by the caller (timing enabled); both
+ * NULL disarms. The next such call disarms whatever it returns; if it
+ * launches nothing, the events are left as they were. With timing armed, a
+ * call on a stream that is capturing a graph returns TQ_E_CAPTURE before
+ * launching anything. Returns TQ_E_NULL when exactly one event is NULL.
+ * Host only: records nothing by itself. */
+int32_t tq_time_next_call(void *start, void *stop);
 
 /* Encode K and V [tokens, heads, head_dim] of dtype `in_dtype` into the
  * planes of `out` (ops.ts encodeKeys + packBits for K, encodeValues +

@@ -42,6 +42,7 @@ EXPORTS = (
     "tq_merge_rows", "tq_extend_rows", "tq_extract_row", "tq_filter_rows",
     "tq_lloyd_max_workspace_bytes", "tq_lloyd_max_fit",
     "tq_attention_workspace_bytes", "tq_attention_decode", "tq_attention_decode_static",
+    "tq_time_next_call",
 )
 
 
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "tq_packed_dim": (i64, [i32, i32]),
             "tq_status_string": (ctypes.c_char_p, [i32]),
+            "tq_time_next_call": (i32, [P, P]),
             "tq_encode_kv": (i32, [P, P, i32, i64, i32, ctypes.POINTER(TQConfig), ctypes.POINTER(TQPackedKV), P]),
             "tq_decode_kv": (i32, [ctypes.POINTER(TQPackedKV), i64, i32, ctypes.POINTER(TQConfig), P, P, i32, i32, P]),
             "tq_unrotate_values": (i32, [P, P, i32, i64, i32, P]),
@@ -109,6 +111,23 @@ def lib() -> ctypes.CDLL:
 
 def status_string(status: int) -> str:
     return lib().tq_status_string(status).decode()
+
+
+def _event_handle(e):
+    """A hipEvent_t as an int: a raw handle, or an object holding one as `ev`."""
+    if e is None:
+        return None
+    ev = getattr(e, "ev", e)
+    return ev.value if isinstance(ev, ctypes.c_void_p) else int(ev)
+
+
+def time_next_call(start, stop) -> None:
+    """Bind two caller-owned HIP events to the start of the first and the
+    end of the last kernel of the next library call on this thread
+    (tq_time_next_call); None, None disarms."""
+    st = lib().tq_time_next_call(_event_handle(start), _event_handle(stop))
+    if st:
+        raise TQError(st, "time_next_call")
 
 
 def packed_dim(dim: int, bits: int) -> int:

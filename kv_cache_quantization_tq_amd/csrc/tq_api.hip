@@ -98,17 +98,21 @@ const void *unrotate_kernel_for(int32_t d, bool bf16)
     }
 }
 
-// launch `fn` with its argument array on the grid for `rows`
+// launch `fn` with its argument array on the grid for `rows` (the codec's
+// calls launch one kernel each)
 int32_t launch(const void *fn, int64_t rows, int32_t d, void **args, void *stream)
 {
     if (fn == nullptr) return TQ_E_BITS;
     const dim3 grid((uint32_t)grid_for(rows, d));
-    if (hipLaunchKernel(fn, grid, dim3(kBlockThreads), args, 0, (hipStream_t)stream) != hipSuccess) return TQ_E_HIP;
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
+    return tq_host::launch_kernel(fn, grid, dim3(kBlockThreads), args, 0, (hipStream_t)stream, true, true);
 }
+
+thread_local tq_host::Timing t_timing;
 
 
 } // namespace
+
+tq_host::Timing &tq_host::armed_timing() { return t_timing; }
 
 // ---------------------------------------------------------------------------
 // C ABI
@@ -134,7 +138,8 @@ const char *tq_status_string(int32_t status)
     case TQ_E_DTYPE: return "dtype must be TQ_F32 or TQ_BF16";
     case TQ_E_SHAPE: return "tokens must be >= 0 and heads >= 1 (row count within range)";
     case TQ_E_HIP: return "HIP runtime error at kernel launch";
-    case TQ_E_CAPTURE: return "batching call needs more than one launch and its stream is capturing a graph";
+    case TQ_E_CAPTURE: return "the stream is capturing a graph (a batching call needing more than one launch, or "
+                              "kernel timing armed)";
     case TQ_E_SCRATCH: return "the call needs more scratch than the library's static buffer (64 MiB) holds";
     default: return "unknown status";
     }
@@ -143,6 +148,7 @@ const char *tq_status_string(int32_t status)
 int32_t tq_encode_kv(const void *k, const void *v, int32_t in_dtype, int64_t tokens, int32_t heads,
                      const tq_config *cfg, const tq_packed_kv *out, void *stream)
 {
+    const tq_host::TimingScope timing;
     if (cfg == nullptr || out == nullptr) return TQ_E_NULL;
     if (!valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
     if (in_dtype != TQ_F32 && in_dtype != TQ_BF16) return TQ_E_DTYPE;
@@ -177,6 +183,7 @@ int32_t tq_encode_kv(const void *k, const void *v, int32_t in_dtype, int64_t tok
 int32_t tq_decode_kv(const tq_packed_kv *in, int64_t tokens, int32_t heads, const tq_config *cfg, void *k_out,
                      void *v_out, int32_t out_dtype, int32_t flags, void *stream)
 {
+    const tq_host::TimingScope timing;
     if (cfg == nullptr || in == nullptr) return TQ_E_NULL;
     if (!valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
     if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_E_DTYPE;
@@ -212,6 +219,7 @@ int32_t tq_decode_kv(const tq_packed_kv *in, int64_t tokens, int32_t heads, cons
 
 int32_t tq_unrotate_values(const void *x, void *out, int32_t dtype, int64_t rows, int32_t head_dim, void *stream)
 {
+    const tq_host::TimingScope timing;
     if (!valid_head_dim(head_dim)) return TQ_E_HEAD_DIM;
     if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_E_DTYPE;
     if (rows < 0 || rows > ((int64_t)1 << 44)) return TQ_E_SHAPE;
@@ -221,6 +229,14 @@ int32_t tq_unrotate_values(const void *x, void *out, int32_t dtype, int64_t rows
     const void *fn = unrotate_kernel_for(head_dim, dtype == TQ_BF16);
     void *args[] = {&x, &out, &rows};
     return launch(fn, rows, head_dim, args, stream);
+}
+
+int32_t tq_time_next_call(void *start, void *stop)
+{
+    if ((start == nullptr) != (stop == nullptr)) return TQ_E_NULL;
+    t_timing.start = static_cast<hipEvent_t>(start);
+    t_timing.stop = static_cast<hipEvent_t>(stop);
+    return TQ_OK;
 }
 
 int32_t tq_lloyd_max_table(int32_t bits, float *centroids, float *boundaries)

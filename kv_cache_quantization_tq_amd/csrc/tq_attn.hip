@@ -1001,6 +1001,7 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
                             float scale, void *out, int32_t out_dtype, void *workspace, int64_t workspace_bytes,
                             void *stream)
 {
+    const tq_host::TimingScope timing;
     const int32_t st = attention_args_status(q, q_dtype, cache, batch, width, kv_heads, q_heads, cfg, scale, out,
                                              out_dtype);
     if (st != TQ_OK) return st;
@@ -1041,9 +1042,9 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
         const int64_t blocks = groups * 8 * kv_heads;
         if (blocks > 0x7fffffff) return TQ_E_SHAPE;
         void *args[] = {&p};
-        if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(kBlockThreads), args, lds_bytes,
-                            (hipStream_t)stream) != hipSuccess)
-            return TQ_E_HIP;
+        const int32_t ls = tq_host::launch_kernel(fn, dim3((uint32_t)blocks), dim3(kBlockThreads), args, lds_bytes,
+                                                  (hipStream_t)stream, true, false);
+        if (ls != TQ_OK) return ls;
     }
     // merge (rows with no split are zeros) and the inverse rotation
     const int64_t rows = (int64_t)batch * q_heads;
@@ -1053,11 +1054,9 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
         uint32_t *o32 = static_cast<uint32_t *>(out);
         int64_t words = rows * d * (out_dtype == TQ_BF16 ? 2 : 4) / 4;
         void *argsz[] = {&o32, &words};
-        if (hipLaunchKernel(reinterpret_cast<const void *>(&attn_zero_kernel),
-                            dim3((uint32_t)((words + kBlockThreads - 1) / kBlockThreads)), dim3(kBlockThreads), argsz,
-                            0, (hipStream_t)stream) != hipSuccess)
-            return TQ_E_HIP;
-        return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
+        return tq_host::launch_kernel(reinterpret_cast<const void *>(&attn_zero_kernel),
+                                      dim3((uint32_t)((words + kBlockThreads - 1) / kBlockThreads)),
+                                      dim3(kBlockThreads), argsz, 0, (hipStream_t)stream, true, true);
     }
     const float *cpart = static_cast<const float *>(workspace);
     int32_t nsp = (int32_t)nch;
@@ -1067,15 +1066,15 @@ int32_t tq_attention_decode(const void *q, int32_t q_dtype, const tq_packed_kv *
                     : d == 128 ? reinterpret_cast<const void *>(&attn_combine_kernel<128>)
                     : d == 256 ? reinterpret_cast<const void *>(&attn_combine_kernel<256>)
                     : reinterpret_cast<const void *>(&attn_combine_kernel<512>);
-    if (hipLaunchKernel(fn2, dim3((uint32_t)rows), dim3(kBlockThreads), args2, 0, (hipStream_t)stream) != hipSuccess)
-        return TQ_E_HIP;
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
+    return tq_host::launch_kernel(fn2, dim3((uint32_t)rows), dim3(kBlockThreads), args2, 0, (hipStream_t)stream,
+                                  false, true);
 }
 
 int32_t tq_attention_decode_static(const void *q, int32_t q_dtype, const tq_packed_kv *cache, int32_t batch,
                                    int64_t width, const int32_t *left_pad, int32_t kv_heads, int32_t q_heads,
                                    const tq_config *cfg, float scale, void *out, int32_t out_dtype, void *stream)
 {
+    const tq_host::TimingScope timing;
     if (cfg == nullptr) return TQ_E_NULL;
     if (!tq_host::valid_head_dim(cfg->head_dim)) return TQ_E_HEAD_DIM;
     const int64_t need = tq_attention_workspace_bytes(batch, kv_heads, q_heads, cfg->head_dim, width);

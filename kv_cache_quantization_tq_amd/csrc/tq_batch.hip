@@ -186,10 +186,10 @@ class Segments {
             const int64_t gx = (most + kChunk - 1) / kChunk;
             if (gx > 0x7fffffff) return TQ_E_SHAPE;
             void *args[] = {&L};
-            if (hipLaunchKernel(reinterpret_cast<const void *>(&segment_copy_kernel), dim3((uint32_t)gx, L.count),
-                                dim3(kThreads), args, 0, (hipStream_t)stream) != hipSuccess)
-                return TQ_E_HIP;
-            if (hipGetLastError() != hipSuccess) return TQ_E_HIP;
+            const int32_t ls = tq_host::launch_kernel(reinterpret_cast<const void *>(&segment_copy_kernel),
+                                                      dim3((uint32_t)gx, L.count), dim3(kThreads), args, 0,
+                                                      (hipStream_t)stream, a == 0, a + (size_t)kMaxSegs >= segs_.size());
+            if (ls != TQ_OK) return ls;
         }
         return TQ_OK;
     }
@@ -217,6 +217,7 @@ extern "C" {
 int32_t tq_merge_rows(const tq_packed_kv *srcs, const int64_t *lens, int32_t n, int64_t width, int32_t heads,
                       const tq_config *cfg, const tq_packed_kv *dst, int64_t *left_pad, void *stream)
 {
+    const tq_host::TimingScope timing;
     if (n < 0 || !token_count_ok(width)) return TQ_E_SHAPE;
     if ((int64_t)n * width > ((int64_t)1 << 40)) return TQ_E_SHAPE;
     if (n > 0 && lens == nullptr) return TQ_E_NULL;
@@ -250,6 +251,7 @@ int32_t tq_extend_rows(const tq_packed_kv *batch, int32_t b, int64_t width, cons
                        const tq_packed_kv *row, int64_t row_len, int64_t new_width, int32_t heads,
                        const tq_config *cfg, const tq_packed_kv *dst, int64_t *left_pad_out, void *stream)
 {
+    const tq_host::TimingScope timing;
     if (b < 0 || !token_count_ok(width) || !token_count_ok(row_len) || !token_count_ok(new_width))
         return TQ_E_SHAPE;
     if (new_width < width || new_width < row_len) return TQ_E_SHAPE;
@@ -287,6 +289,7 @@ int32_t tq_extend_rows(const tq_packed_kv *batch, int32_t b, int64_t width, cons
 int32_t tq_extract_row(const tq_packed_kv *batch, int32_t b, int64_t width, int32_t i, int64_t left_pad,
                        int32_t heads, const tq_config *cfg, const tq_packed_kv *dst, void *stream)
 {
+    const tq_host::TimingScope timing;
     if (b < 1 || i < 0 || i >= b || !token_count_ok(width) || left_pad < 0 || left_pad > width) return TQ_E_SHAPE;
     if ((int64_t)b * width > ((int64_t)1 << 40)) return TQ_E_SHAPE;
     if (width - left_pad == 0) return empty_output_ok(cfg, heads);
@@ -302,6 +305,7 @@ int32_t tq_extract_row(const tq_packed_kv *batch, int32_t b, int64_t width, int3
 int32_t tq_filter_rows(const tq_packed_kv *batch, int32_t b, int64_t width, const int32_t *keep, int32_t n,
                        int32_t heads, const tq_config *cfg, const tq_packed_kv *dst, void *stream)
 {
+    const tq_host::TimingScope timing;
     if (b < 0 || n < 0 || !token_count_ok(width)) return TQ_E_SHAPE;
     if ((int64_t)b * width > ((int64_t)1 << 40) || (int64_t)n * width > ((int64_t)1 << 40)) return TQ_E_SHAPE;
     if (n > 0 && keep == nullptr) return TQ_E_NULL;

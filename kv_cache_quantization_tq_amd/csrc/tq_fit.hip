@@ -35,6 +35,7 @@
 #include <string.h>
 
 #include "tq.h"
+#include "tq_host.h"
 
 namespace {
 
@@ -795,6 +796,7 @@ int32_t tq_lloyd_max_fit(const float *samples, int64_t n, int32_t levels, const 
                          double *centroids, double *boundaries, void *workspace, int64_t workspace_bytes,
                          void *stream)
 {
+    const tq_host::TimingScope timing;
     if (levels < 2 || levels > kMaxLevels) return TQ_E_BITS;
     if (n < 1 || n > kMaxSamples || iterations < 0) return TQ_E_SHAPE;
     if (samples == nullptr || init == nullptr || centroids == nullptr || workspace == nullptr) return TQ_E_NULL;
@@ -822,8 +824,24 @@ int32_t tq_lloyd_max_fit(const float *samples, int64_t n, int32_t levels, const 
     const int64_t want = (n / 4 + kThreads) / kThreads;
     const int64_t cap = 4LL * cus < kMaxBlocks ? 4LL * cus : kMaxBlocks;
     const int grid = (int)(want < cap ? want : cap);
-    hipLaunchKernelGGL(fit_absmax_kernel, dim3(grid), dim3(kThreads), 0, st, samples, n, h);
-    hipLaunchKernelGGL(fit_init_kernel, dim3(1), dim3(kThreads), 0, st, h, grid, n);
+    {
+        const float *a0 = samples;
+        int64_t a1 = n;
+        FitHead *a2 = h;
+        void *args[] = {&a0, &a1, &a2};
+        if ((r = tq_host::launch_kernel(reinterpret_cast<const void *>(&fit_absmax_kernel), dim3(grid),
+                                        dim3(kThreads), args, 0, st, true, false)) != TQ_OK)
+            return r;
+    }
+    {
+        FitHead *a0 = h;
+        int a1 = grid;
+        int64_t a2 = n;
+        void *args[] = {&a0, &a1, &a2};
+        if ((r = tq_host::launch_kernel(reinterpret_cast<const void *>(&fit_init_kernel), dim3(1), dim3(kThreads),
+                                        args, 0, st, false, iterations == 0)) != TQ_OK)
+            return r;
+    }
     if (iterations > 0) {
         const int64_t tiles = (n + kTile - 1) / kTile;
         // four passes: samples -> b -> a -> b -> a
@@ -860,13 +878,15 @@ int32_t tq_lloyd_max_fit(const float *samples, int64_t n, int32_t levels, const 
             hipLaunchKernelGGL(fit_prefix_kernel<false>, dim3(tiles), dim3(kThreads), 0, st, keys_a, n, h, tile_sum,
                                prefix);
         }
-        if (levels <= kSmallLevels) {
-            hipLaunchKernelGGL(fit_iterate_small_kernel, dim3(1), dim3(kIterThreads), 0, st, keys_a, prefix, n, levels,
-                               iterations, h);
-        } else {
-            hipLaunchKernelGGL(fit_iterate_kernel, dim3(1), dim3(kIterThreads), 0, st, keys_a, prefix, n, levels,
-                               iterations, h);
-        }
+        const unsigned int *a0 = keys_a;
+        const long long *a1 = prefix;
+        int64_t a2 = n;
+        int a3 = levels, a4 = iterations;
+        FitHead *a5 = h;
+        void *args[] = {&a0, &a1, &a2, &a3, &a4, &a5};
+        const void *fn = levels <= kSmallLevels ? reinterpret_cast<const void *>(&fit_iterate_small_kernel)
+                                                : reinterpret_cast<const void *>(&fit_iterate_kernel);
+        if ((r = tq_host::launch_kernel(fn, dim3(1), dim3(kIterThreads), args, 0, st, false, true)) != TQ_OK) return r;
     }
     if ((r = hip_ok(hipGetLastError())) != TQ_OK) return r;
     int shift = 0;

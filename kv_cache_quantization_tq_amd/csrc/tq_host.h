@@ -1,8 +1,10 @@
-// tq_host.h -- host-side argument checks shared by the C ABI translation
-// units (tq_api.hip, tq_batch.hip).
+// tq_host.h -- host-side argument checks and the kernel launch shared by the
+// C ABI translation units (tq_api.hip, tq_attn.hip, tq_batch.hip, tq_fit.hip).
 #ifndef TQ_HOST_H
 #define TQ_HOST_H
 
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "tq.h"
@@ -27,6 +29,44 @@ inline int32_t check_rows(int64_t tokens, int32_t heads, int64_t *rows)
     if (tokens > (int64_t)1 << 40 || heads > (1 << 20)) return TQ_E_SHAPE;
     *rows = tokens * heads;
     return TQ_OK;
+}
+
+// Kernel timing armed by tq_time_next_call on the calling host thread; the
+// storage lives in tq_api.hip.
+struct Timing {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+Timing &armed_timing();
+
+// Disarms the timing when an entry point returns, whatever it returns.
+struct TimingScope {
+    TimingScope() = default;
+    TimingScope(const TimingScope &) = delete;
+    TimingScope &operator=(const TimingScope &) = delete;
+    ~TimingScope() { armed_timing() = Timing{}; }
+};
+
+// Launches fn. With timing armed, the start event is bound to this dispatch's
+// start when `first` and the stop event to its end when `last`
+// (hipExtLaunchKernel takes both from the dispatch's own timestamps); a
+// capturing stream then refuses with TQ_E_CAPTURE before anything launches,
+// since every entry point's first launch is a `first` one.
+inline int32_t launch_kernel(const void *fn, dim3 grid, dim3 block, void **args, size_t lds, hipStream_t s,
+                             bool first, bool last)
+{
+    const Timing &t = armed_timing();
+    hipEvent_t a = first ? t.start : nullptr, b = last ? t.stop : nullptr;
+    hipError_t e = hipSuccess;
+    if (a == nullptr && b == nullptr) {
+        e = hipLaunchKernel(fn, grid, block, args, lds, s);
+    } else {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess) return TQ_E_HIP;
+        if (cs != hipStreamCaptureStatusNone) return TQ_E_CAPTURE;
+        e = hipExtLaunchKernel(fn, grid, block, args, lds, s, a, b, 0);
+    }
+    if (e != hipSuccess) return TQ_E_HIP;
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
 }
 
 } // namespace tq_host

@@ -55,6 +55,18 @@ def test_status_strings():
     assert tq.status_string(99) == "unknown status"
 
 
+def test_time_next_call_takes_both_events_or_neither():
+    L = tq.lib()
+    assert L.tq_time_next_call(FAKE, None) == tq.TQ_E_NULL
+    assert L.tq_time_next_call(None, FAKE) == tq.TQ_E_NULL
+    assert L.tq_time_next_call(None, None) == tq.TQ_OK
+    # arming stores the handles only; a call failing validation disarms
+    # without touching them
+    assert L.tq_time_next_call(FAKE, FAKE + 64) == tq.TQ_OK
+    assert _enc(cfg=(100, 4, 4, 0)) == tq.TQ_E_HEAD_DIM
+    assert L.tq_time_next_call(None, None) == tq.TQ_OK
+
+
 def _enc(k=FAKE, v=FAKE, dtype=tq.TQ_BF16, tokens=16, heads=2, cfg=(128, 4, 4, 0), planes=None):
     planes = planes if planes is not None else [FAKE] * 5
     c = tq.TQConfig(*cfg) if cfg is not None else None

@@ -35,10 +35,14 @@ Lloyd-Max, keys 4-bit affine. What one step is:
 
 Inputs are resident in HBM before timing starts. The timed region is
 exactly K steps launched one by one after W warm-up steps, bracketed by
-synchronisations and two HIP events on the launch stream (the step time);
-every kernel call in it is timed by a pair of HIP events that the library
-binds to the start of its first and the end of its last dispatch
-(tq_time_next_call), i.e. device time, as a kernel trace measures it.
+synchronisations and two HIP events on the launch stream (the step time).
+Inside it every kernel call carries a HIP event that the library binds to
+the end of its last dispatch (tq_time_next_call), which adds nothing to the
+launch: a kernel's time is the interval from the previous call's end to its
+own, i.e. its device time plus the dispatch gap ahead of it (the Lloyd fit,
+which waits for the host, from its first dispatch's start). Steps launch
+library calls prepared once (tq.PreparedCall), so that the host keeps ahead
+of the GPU.
 Prints one JSON line: value = KV tokens per second (one KV token = one
 position with K and V of all its heads; for the decode workloads, tokens
 decoded), the roofline of the dominant kernel (algorithmic bytes per
@@ -268,26 +272,50 @@ def cpu_baseline(w, kn, vn, do_encode, do_decode, tokens_per_row):
 # ---------------------------------------------------------------------------
 
 class Timer:
-    """Timing of the timed loop: a pair of HIP events around the whole loop
-    (the step time), and per step and kernel a start/stop pair that the
-    library binds to that kernel's own dispatch (tq_time_next_call), so that
-    a kernel's figure is its device time from start to end, the interval a
-    kernel trace reports."""
+    """Kernel timing inside the timed region. Every kernel call gets a HIP
+    event that the library binds to the end of its last dispatch
+    (tq_time_next_call with a stop event only, which adds nothing to the
+    launch); a call's time is the interval from the end of the call before
+    it (for the first call, the event that opens the region) to its own
+    end: its device time plus the dispatch gap ahead of it, and the calls'
+    times add up to the region's. Calls that wait for the host (the Lloyd
+    fit) are timed from their first dispatch's start instead (`spans`): a
+    start event makes the runtime enqueue a marker ahead of the kernel,
+    which a host-synchronous call does not notice."""
 
-    def __init__(self, torch, steps, names):
+    def __init__(self, torch, steps, names, spans=()):
         stream = ctypes_stream(torch)
         self.start, self.end = HipEvent(stream), HipEvent(stream)
-        self.ev = [{n: (HipEvent(stream), HipEvent(stream)) for n in names} for _ in range(steps)]
+        self.names = list(names)
+        self.spans = set(spans)
+        self.ev = [{n: (HipEvent(stream) if n in self.spans else None, HipEvent(stream)) for n in self.names}
+                   for _ in range(steps)]
 
     def per_kernel_ms(self, name):
-        return [a.elapsed_time(b) for a, b in (row[name] for row in self.ev)]
+        out, prev = [], self.start
+        for row in self.ev:
+            for n in self.names:
+                a, b = row[n]
+                if n == name:
+                    out.append((a if a is not None else prev).elapsed_time(b))
+                prev = b
+        return out
 
 
 def arm(tq, ev, name):
-    """Bind the step's event pair for `name` to the kernels of the next
-    library call (no-op outside the timed loop)."""
+    """Bind the step's events for `name` to the next library call (no-op
+    outside the timed region)."""
     if ev is not None:
         tq.time_next_call(*ev[name])
+
+
+def run(call, stream):
+    """Issue a prepared library call, on `stream` when one is given (the
+    graph capture's stream) or else on the stream it was prepared on. The
+    steps prepare their calls once: the binding's per-call marshalling plus
+    the HIP runtime's cost of a launch with timing events (~8 us) would
+    otherwise pace the launches of the smaller workloads from the host."""
+    return call() if stream is None else call.on(stream)()
 
 
 def ctypes_stream(torch):
@@ -306,17 +334,19 @@ def setup_encode_decode(torch, tq, W, w, dev, sets_hint):
         k = k0 if s == 0 else k0.clone()
         v = v0 if s == 0 else v0.clone()
         planes = tq.empty_planes(w.rows, w.head_dim, w.k_bits, w.v_bits, dev)
-        sets.append((k, v, planes, torch.empty_like(k, dtype=torch.bfloat16),
-                     torch.empty_like(v, dtype=torch.bfloat16)))
+        ko, vo = torch.empty_like(k, dtype=torch.bfloat16), torch.empty_like(v, dtype=torch.bfloat16)
+        sets.append((tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed, out=planes,
+                                  prepare=True),
+                     tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
+                                  k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo, prepare=True)))
     log(f"workload {w.name}: {w.rows} rows, {nsets} buffer sets of {per_set / 2**20:.0f} MiB")
 
-    def step(i, ev=None):
-        k, v, planes, ko, vo = sets[i % nsets]
+    def step(i, ev=None, stream=None):
+        enc, dec = sets[i % nsets]
         arm(tq, ev, "encode")
-        tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed, out=planes)
+        run(enc, stream)
         arm(tq, ev, "decode")
-        tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
-                     k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
+        run(dec, stream)
 
     enc_b, dec_b = row_bytes(w)
     kernels = {"encode": w.rows * enc_b, "decode": w.rows * dec_b}
@@ -340,20 +370,25 @@ def setup_long_decode(torch, tq, W, w, dev, max_steps):
     vo = torch.empty_like(ko)
     row_b = {n: p.shape[1] * p.element_size() for n, p in planes.items()}
     log(f"workload {w.name}: {T} cached tokens x {H} heads, room for {max_steps} appends")
-
-    def step(i, ev=None):
+    calls = []
+    for i in range(max_steps):
         n = T + i  # tokens already cached
         view = {nm: p[n * H:(n + 1) * H] for nm, p in planes.items()}
         nk, nv = appends[i]
+        calls.append((tq.encode_kv(nk, nv, v_bits=w.v_bits, k_bits=w.k_bits, out=view, prepare=True),
+                      tq.decode_kv(planes, tokens=n + 1, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits,
+                                   k_out=ko[: n + 1], v_out=vo[: n + 1], prepare=True)))
+
+    def step(i, ev=None, stream=None):
+        append, dec = calls[i]
         arm(tq, ev, "append")
-        tq.encode_kv(nk, nv, v_bits=w.v_bits, k_bits=w.k_bits, out=view)
+        run(append, stream)
         arm(tq, ev, "decode")
-        tq.decode_kv(planes, tokens=n + 1, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits,
-                     k_out=ko[: n + 1], v_out=vo[: n + 1])
+        run(dec, stream)
 
     enc_b, dec_b = row_bytes(w)
     # decode bytes of the first timed step's cache length (the cache grows by
-    # one token per step: under 0.05% over a run)
+    # one token per step: under 0.1% over a run)
     kernels = {"append": H * enc_b, "decode": (T + 1) * H * dec_b}
     tokens = lambda i: T + i + 1
     cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
@@ -370,11 +405,12 @@ def setup_joint(torch, tq, W, w, dev):
     ko = torch.empty((w.kv_tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     vo = torch.empty_like(ko)
     log(f"workload {w.name}: {w.rows} rows")
+    dec = tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
+                       k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo, prepare=True)
 
-    def step(i, ev=None):
+    def step(i, ev=None, stream=None):
         arm(tq, ev, "decode")
-        tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
-                     k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
+        run(dec, stream)
 
     _, dec_b = row_bytes(w)
     cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
@@ -396,18 +432,18 @@ def setup_decode_only(torch, tq, W, w, dev, sets_hint):
     sets = []
     for s in range(nsets):
         planes = tq.encode_kv(k0, v0, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed)
-        sets.append((planes, torch.empty_like(k0, dtype=torch.bfloat16), torch.empty_like(v0, dtype=torch.bfloat16)))
+        ko, vo = torch.empty_like(k0, dtype=torch.bfloat16), torch.empty_like(v0, dtype=torch.bfloat16)
+        sets.append(tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
+                                 k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo, prepare=True))
     torch.cuda.synchronize()
     ns = min(w.rows, 65536)
     sample = (W.to_oracle(k0.view(-1, w.head_dim)[:ns]), W.to_oracle(v0.view(-1, w.head_dim)[:ns]))
     del k0, v0
     log(f"workload {w.name}: {w.rows} rows, {nsets} plane sets of {per_set / 2**20:.0f} MiB (planes + outputs)")
 
-    def step(i, ev=None):
-        planes, ko, vo = sets[i % nsets]
+    def step(i, ev=None, stream=None):
         arm(tq, ev, "decode")
-        tq.decode_kv(planes, tokens=w.kv_tokens, heads=w.heads, head_dim=w.head_dim, v_bits=w.v_bits,
-                     k_bits=w.k_bits, k_signed=w.k_signed, k_out=ko, v_out=vo)
+        run(sets[i % nsets], stream)
 
     cpu = lambda: cpu_baseline(w, sample[0], sample[1], False, True, 1.0 / w.heads)
     return step, {"decode": w.rows * dec_b}, (lambda i: w.kv_tokens), cpu, \
@@ -426,21 +462,21 @@ def setup_encode_only(torch, tq, W, w, dev, sets_hint):
     for s in range(nsets):
         k = k0 if s == 0 else k0.clone()
         v = v0 if s == 0 else v0.clone()
-        sets.append((k, v, tq.empty_planes(w.rows, w.head_dim, w.k_bits, w.v_bits, dev)))
+        sets.append(tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed,
+                                 out=tq.empty_planes(w.rows, w.head_dim, w.k_bits, w.v_bits, dev), prepare=True))
     torch.cuda.synchronize()
     log(f"workload {w.name}: {w.rows} rows, {nsets} buffer sets of {per_set / 2**20:.0f} MiB (inputs + planes)")
 
-    def step(i, ev=None):
-        k, v, planes = sets[i % nsets]
+    def step(i, ev=None, stream=None):
         arm(tq, ev, "encode")
-        tq.encode_kv(k, v, v_bits=w.v_bits, k_bits=w.k_bits, k_signed=w.k_signed, out=planes)
+        run(sets[i % nsets], stream)
 
     cpu = lambda: cpu_baseline(w, W.to_oracle(k0), W.to_oracle(v0), True, False, 1.0 / w.heads)
     return step, {"encode": w.rows * enc_b}, (lambda i: w.kv_tokens), cpu, \
         {**codec_config(w), "workload": DESCRIPTION[w.name], "buffer_sets": nsets}
 
 
-def setup_deferred_v(torch, tq, W, dev, steps_total):
+def setup_deferred_v(torch, tq, W, dev):
     """Rotated-domain value decode plus one un-rotation of an attention
     output per step; the eager decode (inverse transform for every token) of
     the same cache is timed after the timed region for comparison."""
@@ -459,26 +495,32 @@ def setup_deferred_v(torch, tq, W, dev, steps_total):
     att = torch.randn((1, hq, d), generator=g, device=dev)  # stands for an attention output over rotated values
     att_out = torch.empty_like(att)
     log(f"workload deferred_v: {T} tokens x {H} heads, rotated decode + un-rotation of {hq} rows")
+    dec = tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo,
+                       rotated_v=True, prepare=True)
+    unrot = tq.unrotate_values(att, out=att_out, prepare=True)
+    eager = tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko,
+                         v_out=vo, prepare=True)
 
-    def step(i, ev=None):
+    def step(i, ev=None, stream=None):
         arm(tq, ev, "decode")
-        tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo,
-                     rotated_v=True)
+        run(dec, stream)
         arm(tq, ev, "unrotate")
-        tq.unrotate_values(att, out=att_out)
+        run(unrot, stream)
 
     def eager_us(reps=20):
         """Average device time of the eager decode (values fully decoded),
         timed like the kernels of the timed loop."""
-        ev = [(HipEvent(ctypes_stream(torch)), HipEvent(ctypes_stream(torch))) for _ in range(reps)]
+        t0 = HipEvent(ctypes_stream(torch))
+        ev = [HipEvent(ctypes_stream(torch)) for _ in range(reps)]
         for _ in range(3):
-            tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo)
+            eager()
         torch.cuda.synchronize()
-        for a, b in ev:
-            tq.time_next_call(a, b)
-            tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=w.v_bits, k_bits=w.k_bits, k_out=ko, v_out=vo)
+        t0.record()
+        for b in ev:
+            tq.time_next_call(None, b)
+            eager()
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+        return sum(a.elapsed_time(b) for a, b in zip([t0] + ev[:-1], ev)) / reps * 1e3
 
     def cpu():
         import oracle as O
@@ -533,10 +575,12 @@ def setup_batch_merge(torch, tq, W, dev):
     cfg = TQConfig(d, kb, vb, 0)
     pk = _packed(dst)
 
-    def step(i, ev=None):
+    stream0 = ctypes_stream(torch)
+
+    def step(i, ev=None, stream=None):
         arm(tq, ev, "merge")
         st = tq.lib().tq_merge_rows(srcs, lens_a.ctypes.data, len(lens), width, H, ctypes.byref(cfg),
-                                    ctypes.byref(pk), None, ctypes_stream(torch))
+                                    ctypes.byref(pk), None, stream0 if stream is None else stream)
         if st:
             raise tq.TQError(st, "tq_merge_rows")
 
@@ -567,9 +611,9 @@ def setup_lloyd_fit(torch, tq, W, dev, iterations=500):
     ws = torch.empty(int(tq.lib().tq_lloyd_max_workspace_bytes(n)), dtype=torch.uint8, device=dev)
     log(f"workload lloyd_fit: {n} samples, {levels} levels, {iterations} iterations per step")
 
-    def step(i, ev=None):
+    def step(i, ev=None, stream=None):
         arm(tq, ev, "fit")
-        tq.lloyd_max_fit(x, levels, init, iterations, workspace=ws)
+        tq.lloyd_max_fit(x, levels, init, iterations, workspace=ws, stream=stream)
 
     def cpu():
         import numpy as np
@@ -612,10 +656,12 @@ def setup_attn_decode(torch, tq, W, dev):
     nbytes = T * H * row_b + q.numel() * 2 + out.numel() * 4
     log(f"workload attn_decode: {T} tokens x {H} KV heads, {hq} query heads, {T * H * row_b / 1e6:.1f} MB of cache")
 
-    def step(i, ev=None):
+    attn = tq.attention_decode(q, planes, batch=1, width=T, kv_heads=H, head_dim=d, k_bits=w.k_bits,
+                               v_bits=w.v_bits, out=out, workspace=ws, prepare=True)
+
+    def step(i, ev=None, stream=None):
         arm(tq, ev, "attention")
-        tq.attention_decode(q, planes, batch=1, width=T, kv_heads=H, head_dim=d, k_bits=w.k_bits,
-                            v_bits=w.v_bits, out=out, workspace=ws)
+        run(attn, stream)
 
     def cpu():
         import numpy as np
@@ -692,8 +738,7 @@ def main():
         step, kernels, tokens, cpu_fn, config = setup_joint(torch, tq, W, w, dev)
         config["workload"] = DESCRIPTION["long_k8v3"]
     elif args.workload == "deferred_v":
-        step, kernels, tokens, cpu_fn, config, extra = setup_deferred_v(torch, tq, W, dev,
-                                                                               args.warmup + steps)
+        step, kernels, tokens, cpu_fn, config, extra = setup_deferred_v(torch, tq, W, dev)
     elif args.workload == "long_decode":
         step, kernels, tokens, cpu_fn, config = setup_long_decode(torch, tq, W, w, dev,
                                                                          args.warmup + steps)
@@ -717,14 +762,18 @@ def main():
         log(f"copy calibration: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")
         del src, dst
 
+    # warm-up steps, timed like the timed region (the first launches with
+    # bound events pay a one-time cost)
+    spans = ("fit",)
+    warm = Timer(torch, args.warmup, kernels, spans)
     for i in range(args.warmup):
-        step(i)
+        step(i, warm.ev[i])
     torch.cuda.synchronize()
 
     # the timed region: exactly `steps` steps launched one by one between
-    # two events on the launch stream, each kernel timed by events bound to
-    # its own dispatch
-    tm = Timer(torch, steps, kernels)
+    # two events on the launch stream, every kernel call timed by a stop
+    # event bound to its last dispatch
+    tm = Timer(torch, steps, kernels, spans)
     torch.cuda.synchronize()
     tm.start.record()
     for i in range(steps):
@@ -742,7 +791,7 @@ def main():
     # kernel arguments; the cause is not established)
     graph_ms_per_step = None
     if args.workload not in ("lloyd_fit", "batch_merge") and not args.no_graph:
-        graph = HipGraph(torch, lambda: [step(args.warmup + i) for i in range(steps)])
+        graph = HipGraph(torch, lambda: [step(args.warmup + i, None, ctypes_stream(torch)) for i in range(steps)])
         graph.launch()
         graph.synchronize()
         t0, t1 = HipEvent(graph.stream), HipEvent(graph.stream)

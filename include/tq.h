@@ -113,18 +113,20 @@ const char *tq_status_string(int32_t status);
 
 /* Kernel timing, for callers that measure the kernels (benchmarks): not an
  * operation of the pages. Arms the calling host thread so that the next
- * call of this library that takes a `stream` binds `start` to the start of
- * the first kernel it launches and `stop` to the end of the last one
- * (hipExtLaunchKernel's start and stop events). hipEventElapsedTime(start,
- * stop) then gives the device time from the first kernel's start to the
- * last kernel's end, without the dispatch ahead of the first kernel that an
- * event recorded before the call would include. `start` and `stop` are
- * hipEvent_t handles created and owned by the caller (timing enabled); both
- * NULL disarms. The next such call disarms whatever it returns; if it
- * launches nothing, the events are left as they were. With timing armed, a
- * call on a stream that is capturing a graph returns TQ_E_CAPTURE before
- * launching anything. Returns TQ_E_NULL when exactly one event is NULL.
- * Host only: records nothing by itself. */
+ * call of this library that takes a `stream` binds `stop` to the end of the
+ * last kernel it launches and, if `start` is not NULL, `start` to the
+ * start of the first one (hipExtLaunchKernel's stop and start events).
+ * hipEventElapsedTime(e, stop) from an event e on the same stream then
+ * ends exactly at the call's last kernel; a stop event alone adds nothing
+ * to the launch, while a start event makes the HIP runtime enqueue a marker
+ * ahead of the first kernel (measured: launches a few microseconds further
+ * apart). `start` and `stop` are hipEvent_t handles created and owned by
+ * the caller (timing enabled); both NULL disarms. The next such call
+ * disarms whatever it returns; if it launches nothing, the events are left
+ * as they were. With timing armed, a call on a stream that is capturing a
+ * graph returns TQ_E_CAPTURE before launching anything. Returns TQ_E_NULL
+ * when `start` is given without `stop`. Host only: records nothing by
+ * itself. */
 int32_t tq_time_next_call(void *start, void *stop);
 
 /* Encode K and V [tokens, heads, head_dim] of dtype `in_dtype` into the

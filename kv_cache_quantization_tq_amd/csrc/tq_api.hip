@@ -233,7 +233,7 @@ int32_t tq_unrotate_values(const void *x, void *out, int32_t dtype, int64_t rows
 
 int32_t tq_time_next_call(void *start, void *stop)
 {
-    if ((start == nullptr) != (stop == nullptr)) return TQ_E_NULL;
+    if (start != nullptr && stop == nullptr) return TQ_E_NULL;
     t_timing.start = static_cast<hipEvent_t>(start);
     t_timing.stop = static_cast<hipEvent_t>(stop);
     return TQ_OK;

@@ -55,10 +55,10 @@ def test_status_strings():
     assert tq.status_string(99) == "unknown status"
 
 
-def test_time_next_call_takes_both_events_or_neither():
+def test_time_next_call_needs_a_stop_event_with_a_start_event():
     L = tq.lib()
     assert L.tq_time_next_call(FAKE, None) == tq.TQ_E_NULL
-    assert L.tq_time_next_call(None, FAKE) == tq.TQ_E_NULL
+    assert L.tq_time_next_call(None, FAKE) == tq.TQ_OK
     assert L.tq_time_next_call(None, None) == tq.TQ_OK
     # arming stores the handles only; a call failing validation disarms
     # without touching them

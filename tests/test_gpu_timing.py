@@ -2,7 +2,8 @@
 first and last dispatch of a call give its device time, which lies inside
 events recorded around the call; a timed call's results equal an untimed
 call's bit for bit; with timing armed, a capturing stream is refused before
-anything launches, and the refused call disarms."""
+anything launches, and the refused call disarms. Also the binding's prepared
+calls (arguments marshalled once), through which the benchmark launches."""
 from __future__ import annotations
 
 import numpy as np
@@ -65,6 +66,30 @@ def test_timed_encode_and_decode_at_the_prefill_size():
     assert torch.equal(vo.view(torch.int16), vo0.view(torch.int16))
 
 
+def test_stop_event_alone_ends_at_the_last_kernel():
+    """A stop event alone: the interval from an event recorded before the
+    call to it covers the call (no shorter than the start-bound interval of
+    the same call made again) and ends before an event recorded after it."""
+    T, H, d = 20000, 8, 128
+    print(f"[timing] stop event only, encode of {T} tokens x {H} heads", flush=True)
+    k, v = randn((T, H, d), torch.bfloat16, 41), randn((T, H, d), torch.bfloat16, 42)
+    out = tq.empty_planes(T * H, d, 4, 4, DEV)
+    call = tq.encode_kv(k, v, v_bits=4, k_bits=4, out=out, prepare=True)
+    call()
+    s = torch.cuda.current_stream().cuda_stream
+    before, stop, after = HipEvent(s), HipEvent(s), HipEvent(s)
+    torch.cuda.synchronize()
+    before.record()
+    tq.time_next_call(None, stop)
+    call()
+    after.record()
+    torch.cuda.synchronize()
+    to_stop, total = before.elapsed_time(stop), before.elapsed_time(after)
+    inner, _ = timed(call)
+    assert 0 < to_stop <= total
+    assert to_stop >= 0.5 * inner
+
+
 def test_timed_attention_spans_both_launches():
     T, H, hq, d, kb, vb = 20000, 8, 32, 256, 4, 5
     print(f"[timing] attention, width {T}, {H} KV heads, {hq} query heads, d={d}", flush=True)
@@ -119,3 +144,57 @@ def test_armed_timing_refuses_a_capturing_stream():
     torch.cuda.synchronize()
     for n in ref:
         assert torch.equal(ref[n], out[n]), n
+
+
+def test_prepared_calls_equal_the_keyword_calls():
+    """PreparedCall (arguments marshalled once, as the benchmark's launch
+    loops use it) makes the same C call as the keyword functions: outputs
+    equal bit for bit, eagerly and rebound to a capturing stream."""
+    T, H, d, kb, vb = 3000, 4, 256, 4, 5
+    print(f"[timing] prepared calls, {T} tokens x {H} heads, d={d}", flush=True)
+    k, v = randn((T, H, d), torch.bfloat16, 31), randn((T, H, d), torch.bfloat16, 32)
+    ref = tq.encode_kv(k, v, v_bits=vb, k_bits=kb)
+    kd, vd = tq.decode_kv(ref, tokens=T, heads=H, head_dim=d, v_bits=vb, k_bits=kb, rotated_v=True)
+    q = randn((1, 16, d), torch.bfloat16, 33)
+    args = dict(batch=1, width=T, kv_heads=H, head_dim=d, k_bits=kb, v_bits=vb)
+    ws = torch.empty(int(tq.lib().tq_attention_workspace_bytes(1, H, 16, d, T)), dtype=torch.uint8, device=DEV)
+    att = tq.attention_decode(q, ref, workspace=ws, **args)
+    un = tq.unrotate_values(att)
+
+    planes = tq.empty_planes(T * H, d, kb, vb, DEV)
+    ko, vo = torch.empty_like(kd), torch.empty_like(vd)
+    att2, un2 = torch.empty_like(att), torch.empty_like(un)
+    calls = [tq.encode_kv(k, v, v_bits=vb, k_bits=kb, out=planes, prepare=True),
+             tq.decode_kv(planes, tokens=T, heads=H, head_dim=d, v_bits=vb, k_bits=kb, rotated_v=True, k_out=ko,
+                          v_out=vo, prepare=True),
+             tq.attention_decode(q, planes, out=att2, workspace=ws, prepare=True, **args),
+             tq.unrotate_values(att2, out=un2, prepare=True)]
+    assert all(isinstance(c, tq.PreparedCall) for c in calls)
+
+    def check():
+        torch.cuda.synchronize()
+        for n in ref:
+            assert torch.equal(ref[n], planes[n]), n
+        assert torch.equal(ko.view(torch.int16), kd.view(torch.int16))
+        assert torch.equal(vo.view(torch.int16), vd.view(torch.int16))
+        assert torch.equal(att2.view(torch.int32), att.view(torch.int32))
+        assert torch.equal(un2.view(torch.int32), un.view(torch.int32))
+
+    def clear():
+        for t in (*planes.values(), ko, vo, att2, un2):
+            t.zero_()
+        torch.cuda.synchronize()
+
+    for c in calls:
+        c()
+    check()
+    clear()
+    g = HipGraph(torch, lambda: [c.on(torch.cuda.current_stream().cuda_stream)() for c in calls])
+    try:
+        for _ in range(2):
+            g.launch()
+            g.synchronize()
+            check()
+            clear()
+    finally:
+        g.close()

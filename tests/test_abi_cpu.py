@@ -174,6 +174,22 @@ def test_kernel_bin_search_equals_oracle_count(bits):
     np.testing.assert_array_equal(tq.value_bin_host(bits, z), O.bin_index(z, bits))
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+def test_kernel_bin_search_stays_in_its_table_for_nan(bits):
+    """NaN inputs are outside the method (their bins are unspecified), but
+    the bin search is the encoder's only data-dependent address (a table
+    lookup): for NaN of either sign and any payload it must still give an
+    index inside the table. The kernels run this general search for every
+    group whose sum of squares is not finite, which any NaN or infinity in
+    the group makes it."""
+    payloads = np.array([0x7FC00000, 0x7F800001, 0x7FFFFFFF, 0xFFC00000, 0xFF800001, 0xFFFFFFFF, 0x7FA5A5A5],
+                        np.uint32)
+    z = payloads.view(np.float32)
+    assert np.isnan(z).all()
+    idx = tq.value_bin_host(bits, z)
+    assert idx.dtype == np.uint8 and (idx.astype(np.int64) <= (1 << bits) - 1).all()
+
+
 def test_kernel_quotient_equals_ieee_division():
     """The quotient the kernels take for key scales, zero points and codes
     (host build of the same code) equals IEEE binary32 division bit for bit,

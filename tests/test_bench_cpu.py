@@ -2,7 +2,8 @@
 events only, a call's time runs from the previous call's end to its own, so
 the calls of the timed region add up to its length; a call with a start
 event (the Lloyd fit) is timed from that start; arm() hands the right
-events to the library."""
+events to the library; the oracle baseline's passes repeat until their time
+is spent."""
 import bench
 
 
@@ -60,3 +61,10 @@ def test_arm_passes_the_step_events():
     bench.arm(FakeTQ, ev, "fit")
     bench.arm(FakeTQ, None, "encode")  # outside the timed region: nothing
     assert calls == [(None, "stop-e"), ("start-f", "stop-f")]
+
+
+def test_passes_run_until_the_time_is_spent():
+    t = iter([0.3, 0.3, 0.3, 0.3, 0.3])
+    assert bench._passes(lambda: next(t), min_s=1.0) == (0.3, 4)
+    assert bench._passes(lambda: 2.0, min_s=1.0) == (2.0, 1)
+    assert bench._passes(lambda: 0.01, min_s=1.0, max_passes=16) == (0.01, 16)

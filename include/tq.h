@@ -34,7 +34,8 @@
  *
  * Ownership and execution. Every pointer except `cfg`, `out`/`in`
  * (host structs read during the call) is device memory owned by the caller.
- * The library allocates nothing and keeps no per-call state. Calls enqueue
+ * The library allocates nothing and keeps no per-call state (beyond the
+ * events tq_time_next_call arms for the calling thread). Calls enqueue
  * kernels on `stream` (a hipStream_t; NULL is the default stream) and return
  * without waiting. Argument errors are detected on the host before any
  * launch and leave every buffer untouched; a failed launch returns

@@ -1063,13 +1063,15 @@ __device__ __forceinline__ void load_group_codes(const uint8_t *__restrict__ kc,
     }
 }
 
-// Tile loop of the decoder for one key mode (KB = 0: values only).
-template <int D, int VB, int KB, bool KS, bool BF16OUT>
+// Tile loop of the decoder for one key mode (KB = 0: values only). setup()
+// puts the block's centroid table into LDS and waits for the block; every
+// wavefront calls it once, after its first tile's loads.
+template <int D, int VB, int KB, bool KS, bool BF16OUT, typename Setup>
 __device__ __forceinline__ void decode_loop(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks,
                                             const uint16_t *__restrict__ kz, const uint8_t *__restrict__ vc,
                                             const uint16_t *__restrict__ vs, int64_t rows, int32_t rotated,
                                             void *__restrict__ kout, void *__restrict__ vout, const float *cent,
-                                            uint4 *stage)
+                                            uint4 *stage, Setup &&setup)
 {
     constexpr int G = D / kGroup;
     constexpr int RPW = kWave / G;
@@ -1083,9 +1085,7 @@ __device__ __forceinline__ void decode_loop(const uint8_t *__restrict__ kc, cons
     const bool hasv = vout != nullptr;
     const int64_t tiles = (rows + RPW - 1) / RPW;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave; t < tiles; t += stride) {
-        GroupCodes<KB, VB> cur;
-        load_group_codes<D, VB, KB>(kc, ks, kz, vc, vs, t * RPW + rl, rows, g, hasv, cur);
+    auto tile = [&](int64_t t, const GroupCodes<KB, VB> &cur) {
         const int64_t row0 = t * RPW;
         if constexpr (HASK) {
             float y[kGroup];
@@ -1108,6 +1108,22 @@ __device__ __forceinline__ void decode_loop(const uint8_t *__restrict__ kc, cons
             if (!rotated) hadamard<D>(y, rot);
             store_tile<D, BF16OUT>(vout, row0, rows, smask, y, stage);
         }
+    };
+    // the first tile's codes are requested before the block's table reaches
+    // LDS (setup() stores it and waits for the block), so that the two
+    // latencies overlap (long-context decode 266-269 against 278 us); a
+    // wavefront without a tile loads the last row and stores nothing
+    const int64_t t0 = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    {
+        GroupCodes<KB, VB> cur;
+        load_group_codes<D, VB, KB>(kc, ks, kz, vc, vs, t0 * RPW + rl, rows, g, hasv, cur);
+        setup();
+        if (t0 < tiles) tile(t0, cur);
+    }
+    for (int64_t t = t0 + stride; t < tiles; t += stride) {
+        GroupCodes<KB, VB> cur;
+        load_group_codes<D, VB, KB>(kc, ks, kz, vc, vs, t * RPW + rl, rows, g, hasv, cur);
+        tile(t, cur);
     }
 }
 
@@ -1125,22 +1141,54 @@ decode_kernel(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks, c
 {
     constexpr int NC = 1 << VB;
     using S = Stage<BF16OUT>;
+    constexpr int NL = (NC + kBlockThreads - 1) / kBlockThreads;
     __shared__ float cent[NC];
     __shared__ uint4 stage_all[kWavesPerBlock * S::WORDS];
-    if (vout != nullptr) {
+    // the centroids go to registers first (their loads leave before the
+    // first tile's), then to LDS in setup()
+    const bool tables = vout != nullptr; // uniform over the block
+    float cv[NL];
+    if (tables) {
         const float *src = dev_cent<VB>();
-        for (int i = threadIdx.x; i < NC; i += kBlockThreads) cent[i] = src[i];
-        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int i = threadIdx.x + k * kBlockThreads;
+            cv[k] = src[i < NC ? i : NC - 1];
+        }
     }
+    auto setup = [&] {
+        if (tables) {
+#pragma unroll
+            for (int k = 0; k < NL; ++k) {
+                const int i = threadIdx.x + k * kBlockThreads;
+                if (i < NC) cent[i] = cv[k];
+            }
+            __syncthreads();
+        }
+    };
     uint4 *stage = stage_all + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * S::WORDS;
     switch (kmode) {
-    case 2: decode_loop<D, VB, 2, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
-    case 3: decode_loop<D, VB, 3, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
-    case 4: decode_loop<D, VB, 4, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
-    case 5: decode_loop<D, VB, 5, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
-    case 8: decode_loop<D, VB, 8, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
-    case 8 | 16: decode_loop<D, VB, 8, true, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
-    default: decode_loop<D, VB, 0, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage); break;
+    case 2:
+        decode_loop<D, VB, 2, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage, setup);
+        break;
+    case 3:
+        decode_loop<D, VB, 3, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage, setup);
+        break;
+    case 4:
+        decode_loop<D, VB, 4, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage, setup);
+        break;
+    case 5:
+        decode_loop<D, VB, 5, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage, setup);
+        break;
+    case 8:
+        decode_loop<D, VB, 8, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage, setup);
+        break;
+    case 8 | 16:
+        decode_loop<D, VB, 8, true, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage, setup);
+        break;
+    default:
+        decode_loop<D, VB, 0, false, BF16OUT>(kc, ks, kz, vc, vs, rows, rotated, kout, vout, cent, stage, setup);
+        break;
     }
 }
 

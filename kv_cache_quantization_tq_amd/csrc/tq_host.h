@@ -48,23 +48,21 @@ struct TimingScope {
 
 // Launches fn. With timing armed, the start event is bound to this dispatch's
 // start when `first` and the stop event to its end when `last`
-// (hipExtLaunchKernel takes both from the dispatch's own timestamps); a
-// capturing stream then refuses with TQ_E_CAPTURE before anything launches,
-// since every entry point's first launch is a `first` one.
+// (hipExtLaunchKernel takes both from the dispatch's own timestamps). With
+// any event armed, a capturing stream is refused with TQ_E_CAPTURE at the
+// entry point's first launch (a `first` one), before anything launches.
 inline int32_t launch_kernel(const void *fn, dim3 grid, dim3 block, void **args, size_t lds, hipStream_t s,
                              bool first, bool last)
 {
     const Timing &t = armed_timing();
-    hipEvent_t a = first ? t.start : nullptr, b = last ? t.stop : nullptr;
-    hipError_t e = hipSuccess;
-    if (a == nullptr && b == nullptr) {
-        e = hipLaunchKernel(fn, grid, block, args, lds, s);
-    } else {
+    if (first && (t.start != nullptr || t.stop != nullptr)) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(s, &cs) != hipSuccess) return TQ_E_HIP;
         if (cs != hipStreamCaptureStatusNone) return TQ_E_CAPTURE;
-        e = hipExtLaunchKernel(fn, grid, block, args, lds, s, a, b, 0);
     }
+    hipEvent_t a = first ? t.start : nullptr, b = last ? t.stop : nullptr;
+    const hipError_t e = (a == nullptr && b == nullptr) ? hipLaunchKernel(fn, grid, block, args, lds, s)
+                                                        : hipExtLaunchKernel(fn, grid, block, args, lds, s, a, b, 0);
     if (e != hipSuccess) return TQ_E_HIP;
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_E_HIP;
 }

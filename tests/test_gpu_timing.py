@@ -198,3 +198,55 @@ def test_prepared_calls_equal_the_keyword_calls():
             clear()
     finally:
         g.close()
+
+
+def test_stop_event_alone_refuses_capture_before_any_launch():
+    """Armed with a stop event only, a two-launch call (attention) on a
+    capturing stream returns TQ_E_CAPTURE before its first launch: the
+    captured graph holds no node."""
+    import ctypes
+    import gc
+
+    from kv_cache_quantization_tq_amd.hiprt import HIP_STREAM_CAPTURE_MODE_GLOBAL, HIP_STREAM_NON_BLOCKING, hip
+
+    T, H, hq, d = 2000, 4, 16, 128
+    print("[timing] stop event only, attention under stream capture", flush=True)
+    cache = tq.encode_kv(randn((T, H, d), torch.bfloat16, 51), randn((T, H, d), torch.bfloat16, 52),
+                         v_bits=4, k_bits=4)
+    q = randn((1, hq, d), torch.bfloat16, 53)
+    ws = torch.empty(int(tq.lib().tq_attention_workspace_bytes(1, H, hq, d, T)), dtype=torch.uint8, device=DEV)
+    out = torch.empty((1, hq, d), device=DEV)
+    call = tq.attention_decode(q, cache, batch=1, width=T, kv_heads=H, head_dim=d, k_bits=4, v_bits=4, out=out,
+                               workspace=ws, prepare=True)
+    L = hip()
+    L.hipGraphGetNodes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
+    s = ctypes.c_void_p()
+    assert L.hipStreamCreateWithFlags(ctypes.byref(s), HIP_STREAM_NON_BLOCKING) == 0
+    stop = HipEvent(s.value)
+    on_s = call.on(s.value)
+    torch.cuda.synchronize()
+    graph = ctypes.c_void_p()
+    status = None
+    gc.collect()
+    gc.disable()  # no destructor may call the runtime during a global-mode capture
+    try:
+        assert L.hipStreamBeginCapture(s, HIP_STREAM_CAPTURE_MODE_GLOBAL) == 0
+        try:
+            tq.time_next_call(None, stop)
+            on_s()
+        except tq.TQError as e:
+            status = e.status
+        finally:
+            end = L.hipStreamEndCapture(s, ctypes.byref(graph))
+    finally:
+        gc.enable()
+    try:
+        assert end == 0
+        assert status == tq.TQ_E_CAPTURE
+        n = ctypes.c_size_t(99)
+        assert L.hipGraphGetNodes(graph, None, ctypes.byref(n)) == 0
+        assert n.value == 0
+    finally:
+        if graph:
+            L.hipGraphDestroy(graph)
+        L.hipStreamDestroy(s)

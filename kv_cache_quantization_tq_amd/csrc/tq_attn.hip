@@ -606,12 +606,31 @@ __device__ __forceinline__ void wave_tiles(const AttnParams &p, int b, int j, in
         }
     };
 
-    for (int64_t t0 = t_lo; t0 < t_end; t0 += kTile) {
+    // Issue priority falls as the wavefront gets through its range (at 1/2,
+    // 3/4 and 7/8 of its tiles). Each SIMD holds one wavefront of each of
+    // the blocks on its CU, all with equal work, and the arbiter otherwise
+    // favours the oldest: the first blocks dispatched ran ahead and finished
+    // early, leaving the last ones to run with fewer wavefronts to hide
+    // their loads. A wavefront with more tiles left now wins the arbitration
+    // over one further on, so they finish closer together.
+    const int n = (int)((t_end - t_lo + kTile - 1) / kTile);
+    const int q1 = n / 2, q2 = 3 * n / 4, q3 = 7 * n / 8;
+    int i = 0;
+    for (int64_t t0 = t_lo; t0 < t_end; t0 += kTile, ++i) {
+        if (i == 0)
+            __builtin_amdgcn_s_setprio(3);
+        else if (i == q1)
+            __builtin_amdgcn_s_setprio(2);
+        else if (i == q2)
+            __builtin_amdgcn_s_setprio(1);
+        else if (i == q3)
+            __builtin_amdgcn_s_setprio(0);
         KQ kq;
         VRaw<D, VB> vr;
         load_keys(t0, kq);
         tile(t0, kq, vr);
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // Dynamic LDS of a partial block: the query terms [q_terms][kQRows][D + 8]

@@ -678,31 +678,6 @@ attn_partial_kernel(AttnParams p)
     const int b = cg / p.nsplit, c = cg % p.nsplit;
     const int gq = p.g, hq = p.hkv * p.g;
     const int tid = threadIdx.x;
-    const float *cent = dev_cent<VB>();
-    if constexpr (kPairTable<VB>) {
-        float2 *t2 = reinterpret_cast<float2 *>(tab);
-        for (int i = tid; i < (1 << (2 * VB)); i += kBlockThreads)
-            t2[i] = make_float2(cent[i & ((1 << VB) - 1)], cent[i >> VB]);
-    } else {
-        float *t1 = reinterpret_cast<float *>(tab);
-        for (int i = tid; i < (1 << VB); i += kBlockThreads) t1[i] = cent[i];
-    }
-    for (int i = tid; i < kQRows * D; i += kBlockThreads) {
-        const int e = i / D, k = i % D;
-        float xq = 0.0f;
-        if (e < gq) {
-            const int64_t qi = ((int64_t)b * hq + j * gq + e) * D + k;
-            xq = p.q_bf16 ? as_f((uint32_t)reinterpret_cast<const uint16_t *>(p.q)[qi] << 16)
-                          : reinterpret_cast<const float *>(p.q)[qi];
-        }
-        for (int t = 0; t < p.q_terms; ++t) {
-            const uint32_t w = pack_bf16x2(xq, 0.0f);
-            qlds[(t * kQRows + e) * QR + k] = (uint16_t)w;
-            xq -= bf16_lo(w);
-        }
-    }
-    __syncthreads();
-
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int h = lane & 15, g = lane >> 4;
@@ -710,6 +685,79 @@ attn_partial_kernel(AttnParams p)
     const int64_t w0 = ((int64_t)c * kWavesPerBlock + wave) * p.wave_tokens;
     const int64_t t_lo = w0 > pad ? w0 : pad;
     const int64_t t_end = w0 + p.wave_tokens < p.width ? w0 + p.wave_tokens : p.width;
+    // The loads of the block's table copy, then those of its query copy, are
+    // issued in groups ahead of their LDS writes (loops that wrote each
+    // load's data before the next load took a memory round trip per step).
+    const float *cent = dev_cent<VB>();
+    constexpr int NT = kPairTable<VB> ? 1 << (2 * VB) : 1 << VB; // table entries
+    constexpr int TK = (NT + kBlockThreads - 1) / kBlockThreads;
+    float c0[TK], c1[TK];
+#pragma unroll
+    for (int k = 0; k < TK; ++k) {
+        const int i = tid + k * kBlockThreads < NT ? tid + k * kBlockThreads : 0;
+        c0[k] = cent[kPairTable<VB> ? i & ((1 << VB) - 1) : i];
+        c1[k] = kPairTable<VB> ? cent[i >> VB] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < TK; ++k) {
+        const int i = tid + k * kBlockThreads;
+        if (i < NT) {
+            if constexpr (kPairTable<VB>)
+                reinterpret_cast<float2 *>(tab)[i] = make_float2(c0[k], c1[k]);
+            else
+                reinterpret_cast<float *>(tab)[i] = c0[k];
+        }
+    }
+    // the query rows of the group (zeros beyond it), 8 elements per thread
+    // and step
+    constexpr int D8 = D / 8, QN = kQRows * D8, QK = (QN + kBlockThreads - 1) / kBlockThreads;
+    uint4 qw[QK][2];
+#pragma unroll
+    for (int k = 0; k < QK; ++k) {
+        const int i = tid + k * kBlockThreads, e = i / D8, k8 = (i % D8) * 8;
+        qw[k][0] = qw[k][1] = make_uint4(0u, 0u, 0u, 0u);
+        if (i < QN && e < gq) {
+            const int64_t qi = ((int64_t)b * hq + j * gq + e) * D + k8;
+            if (p.q_bf16) {
+                qw[k][0] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.q) + qi);
+            } else {
+                qw[k][0] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(p.q) + qi);
+                qw[k][1] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(p.q) + qi + 4);
+            }
+        }
+    }
+    // as q_terms bf16 terms (a bf16 query is its one term)
+#pragma unroll
+    for (int k = 0; k < QK; ++k) {
+        const int i = tid + k * kBlockThreads, e = i / D8, k8 = (i % D8) * 8;
+        if (i >= QN) continue;
+        float xq[8];
+        if (p.q_bf16) {
+            const uint32_t w[4] = {qw[k][0].x, qw[k][0].y, qw[k][0].z, qw[k][0].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                xq[2 * u] = bf16_lo(w[u]);
+                xq[2 * u + 1] = bf16_hi(w[u]);
+            }
+        } else {
+            const uint32_t w[8] = {qw[k][0].x, qw[k][0].y, qw[k][0].z, qw[k][0].w,
+                                   qw[k][1].x, qw[k][1].y, qw[k][1].z, qw[k][1].w};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) xq[u] = as_f(w[u]);
+        }
+        for (int t = 0; t < p.q_terms; ++t) {
+            uint32_t w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                w[u] = pack_bf16x2(xq[2 * u], xq[2 * u + 1]);
+                xq[2 * u] -= bf16_lo(w[u]);
+                xq[2 * u + 1] -= bf16_hi(w[u]);
+            }
+            *reinterpret_cast<uint4 *>(&qlds[(t * kQRows + e) * QR + k8]) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+    __syncthreads();
+
     const uint16_t *qrow = qlds + (h < gq ? h : kAttnMaxG) * QR + g * (D / 4);
 
     f32x4_t acc[NS];

@@ -113,6 +113,13 @@ def test_many_chunks_and_dtypes(dev):
     case(dev, d=64, kb=8, vb=2, ks=True, g=8, width=2100, seed=6, scale=0.05)
 
 
+@pytest.mark.parametrize("d,g", [(512, 8), (64, 1)])
+def test_bf16_query_at_the_extreme_head_dims(dev, d, g):
+    # the block copies the group's query rows 8 elements per thread: three
+    # such steps per thread at d = 512, one at d = 64
+    case(dev, d=d, kb=4, vb=8 if d == 512 else 3, g=g, width=900, seed=40 + g, q_bf16=True)
+
+
 def test_empty_cache_gives_zeros(dev):
     q = torch.randn(2, 4, 128, device=dev)
     planes = tq.empty_planes(0, 128, 4, 4, dev)

@@ -770,9 +770,10 @@ attn_partial_kernel(AttnParams p)
         wave_tiles<D, VB, KB, KS, kMaxQTerms>(p, b, j, t_lo, t_end, tab, qrow, acc, m_run, l_run);
 
     // merge the block's four wavefront splits: each scales its sums to the
-    // block's maximum, then wavefronts 2 and 3 hand theirs to 0 and 1, and
-    // 1 to 0, through two slots of [head][dim] floats (dim W m + n at
-    // n * 16 + m) over the query terms, which the tiles no longer use
+    // block's maximum, wavefronts 2 and 3 hand theirs to 0 and 1 through two
+    // slots of [head][dim] floats (dim W m + n at n * 16 + m) over the query
+    // terms, which the tiles no longer use, 0 and 1 leave their sums there,
+    // and the block writes the row (a0 + a2) + (a1 + a3) from both slots
     l_run = rows_sum(l_run);
     if (h < gq && g == 0) {
         ml[wave][h][0] = m_run;
@@ -796,27 +797,19 @@ attn_partial_kernel(AttnParams p)
     }
     __syncthreads();
     if (wave < 2 && mine) {
-#pragma unroll
-        for (int n = 0; n < NS; ++n) acc[n] += *reinterpret_cast<const f32x4_t *>(&own[h * SR + n * 16 + 4 * g]);
-    }
-    __syncthreads();
-    if (wave == 1 && mine) {
-#pragma unroll
-        for (int n = 0; n < NS; ++n) *reinterpret_cast<f32x4_t *>(&slot0[h * SR + n * 16 + 4 * g]) = acc[n];
-    }
-    __syncthreads();
-    if (wave == 0 && mine) {
+        // each lane reads and rewrites only its own positions
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
-            acc[n] += *reinterpret_cast<const f32x4_t *>(&slot0[h * SR + n * 16 + 4 * g]);
-            *reinterpret_cast<f32x4_t *>(&slot1[h * SR + n * 16 + 4 * g]) = acc[n];
+            f32x4_t *q = reinterpret_cast<f32x4_t *>(&own[h * SR + n * 16 + 4 * g]);
+            *q = acc[n] + *q;
         }
     }
     __syncthreads();
     for (int i = tid; i < gq * D; i += kBlockThreads) {
         const int e = i / D, k = i % D;
         float *row = part_row<D>(p, b, j * gq + e, c);
-        row[k] = slot1[e * SR + (k % W) * 16 + k / W];
+        const int at = e * SR + (k % W) * 16 + k / W;
+        row[k] = slot0[at] + slot1[at];
         if (k == 0) {
             float M = ml[0][e][0];
 #pragma unroll
